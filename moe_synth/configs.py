@@ -1,0 +1,56 @@
+"""Synthetic workloads for the routed-experts decode step.
+
+Each workload is named by what it is. Shapes follow the pages' decode step of
+a 2/3-bit mixed-K routed-expert pack (lna-lab README, "What is in the pack":
+43 routed layers, EXL3 2/3 bit mixed; LNA-CANON, "制式": TP8, 4 streams with
+3 speculative tokens, i.e. 16 rows per step) and the NVFP4 MLP format of
+"V100 換引擎", section 4.0.
+
+This module holds sizes and recipe switches only; it computes nothing.
+"""
+from dataclasses import dataclass, field
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    config_id: int          # seed namespace, see moe_synth.gen
+    num_experts: int
+    top_k: int
+    hidden: int
+    inter: int
+    fmt: str                # "codebook" or "nvfp4"
+    bits_mix: str           # "all2" | "alternate" | "mix62" | "nvfp4"
+    router: str             # "normal" | "zipf"
+    token_counts: Tuple[int, ...]
+    layers: int = 1
+    zipf_s: float = 1.1
+
+    @property
+    def max_tokens(self) -> int:
+        return max(self.token_counts)
+
+
+WORKLOADS = {
+    # 8 experts, top-2, hidden 256, expert intermediate 128, 2-bit codes.
+    "tiny": Workload("tiny", 1, 8, 2, 256, 128, "codebook", "all2", "normal", (1,)),
+    # One rank's share of an 8-way tensor-parallel layer: I = 2048 / 8.
+    "rank_share": Workload("rank_share", 2, 256, 8, 4096, 256, "codebook", "alternate",
+                           "normal", (1, 4)),
+    # The unsharded layer with Zipf-skewed routing.
+    "full_layer": Workload("full_layer", 3, 256, 8, 4096, 2048, "codebook", "mix62", "zipf",
+                           (1, 2, 4, 8, 16, 24)),
+    # 43 such layers back to back at the 16-row decode batch.
+    "stack43": Workload("stack43", 4, 256, 8, 4096, 2048, "codebook", "mix62", "zipf",
+                        (16,), layers=43),
+    # NVFP4 experts (e2m1 values, e4m3 per-16 scales, fp32 tensor scale).
+    "nvfp4": Workload("nvfp4", 5, 256, 8, 4096, 2048, "nvfp4", "nvfp4", "normal", (2, 8)),
+}
+
+
+def small_workload(name, num_experts, top_k, hidden, inter, fmt="codebook",
+                   bits_mix="alternate", router="normal", config_id=100):
+    """A reduced shape for fast tests (same recipe, smaller sizes)."""
+    return Workload(name, config_id, num_experts, top_k, hidden, inter, fmt, bits_mix,
+                    router, (1,))
