@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-experts decode step on one MI355X.
+
+Default workload: the 43-layer decode-step stack (each layer: 256 experts,
+top-8, hidden 4096, expert intermediate 2048, 2/3-bit mixed codes with 62.5 %
+3-bit experts, Zipf-skewed routing), m = 16 tokens (4 streams x (1 + 3
+speculative tokens)), all 43 layers captured in one HIP graph on one stream.
+One step = one graph replay = one pass of the whole path over all layers.
+The stack streams ~11.8 GB of weights per step, far beyond the 256 MB
+Infinity Cache, so every layer reads its weights cold from HBM.
+
+Prints one JSON line. `value` is the achieved HBM throughput over the
+algorithmic weight bytes of the step (stored codes + scales + codebooks of
+every hit expert, each counted once per layer) divided by the step time.
+`roofline` reports the dominant kernel (the expert kernel) timed alone with
+HIP events recorded on its stream; `cpu_baseline` times the CPU oracle on a
+bounded sample (one layer of the same workload).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-MoE decode µs/launch + achieved HBM GB/s of weight bytes, m=1–24"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack43",
+                    choices=["stack43", "full_layer", "rank_share", "nvfp4", "tiny"])
+    ap.add_argument("--m", type=int, default=None, help="tokens per step (default: workload's)")
+    ap.add_argument("--layers", type=int, default=None, help="layers of the stack (default 43)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-passes", type=int, default=3)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_quantized_moe_block_amd import DeviceLayer
+    from moe_synth import WORKLOADS, gen
+
+    w = WORKLOADS[args.workload]
+    m = args.m or (16 if args.workload in ("stack43", "full_layer") else w.max_tokens)
+    n_layers = args.layers or (w.layers if args.workload == "stack43" else 1)
+    stacked = n_layers > 1
+    dev = torch.device("cuda")
+    torch.cuda.init()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} ({props.multi_processor_count} CUs), workload {w.name}, "
+        f"layers {n_layers}, m {m}")
+
+    # ---- generate and upload every layer (weights + one batch of inputs each)
+    t0 = time.time()
+    layers, inputs, routing_ids = [], [], []
+    for l in range(n_layers):
+        d = gen.make_layer(w, l)
+        d["workload"] = w
+        layer = DeviceLayer.from_case(d, max_tokens=max(m, 1))
+        x = torch.from_numpy(gen.make_x(w, l, m).view(np.int16)).to(dev)
+        lg = torch.from_numpy(gen.make_logits(w, l, m)).to(dev)
+        out = torch.empty(m, w.hidden, device=dev)
+        layers.append(layer)
+        inputs.append((x, lg, out))
+        del d
+        if l % 8 == 0:
+            log(f"layer {l} resident ({time.time() - t0:.1f} s)")
+    info = layers[0].info()
+    log(f"expert grid {info.grid_blocks} blocks ({info.blocks_per_cu}/CU), "
+        f"k-splits {info.k_split_gate_up}/{info.k_split_down}")
+
+    stream = torch.cuda.Stream()
+    # ---- one eager pass (binds handles to the stream, gives the routing)
+    with torch.cuda.stream(stream):
+        for layer, (x, lg, out) in zip(layers, inputs):
+            layer.run(x, lg, out, stream=stream)
+    stream.synchronize()
+    weight_bytes = []
+    hit = []
+    for layer in layers:
+        b = layer.buckets(m)
+        experts = np.nonzero(b["counts"])[0]
+        hit.append(len(experts))
+        weight_bytes.append(layer.weight_bytes(experts))
+        st = layer.stats()
+        assert st.error_word == 0 and st.items_done == st.items, "expert kernel incomplete"
+    step_bytes = float(sum(weight_bytes))
+    log(f"weight bytes per step {step_bytes / 1e9:.3f} GB, hit experts/layer "
+        f"{np.mean(hit):.1f}")
+
+    # ---- capture the whole step in one graph
+    scrub = None
+    if stacked:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for layer, (x, lg, out) in zip(layers, inputs):
+                layer.run(x, lg, out, stream=stream)
+
+        def step():
+            g.replay()
+    else:
+        # single layer: scrub 1 GiB before each launch so weights come from HBM
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        layer, (x, lg, out) = layers[0], inputs[0]
+
+        def step():
+            scrub.zero_()
+            layer.run(x, lg, out, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    stream.synchronize()
+
+    # ---- timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    if stacked:
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(args.steps):
+                step()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    else:
+        # time only the layer, not the scrub
+        per = []
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                scrub.zero_()
+                ev0.record(stream)
+                layer.run(x, lg, out, stream=stream)
+                ev1.record(stream)
+                ev1.synchronize()
+                per.append(ev0.elapsed_time(ev1))
+        ms_per_step = float(np.median(per))
+    wall = (time.perf_counter() - wall0) / args.steps * 1e3
+    torch.cuda.synchronize()
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    us_per_layer = ms_per_step * 1e3 / n_layers
+    log(f"step {ms_per_step:.3f} ms (wall {wall:.3f} ms), {us_per_layer:.1f} us/layer, "
+        f"{value:.0f} GB/s")
+
+    # ---- dominant kernel alone: HIP events around the expert kernel
+    import bit_quantized_moe_block_amd as B
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers]
+    for layer, (eb, ee) in zip(layers, evs):
+        B.moe_decode_profile_events(layer.handle, eb.cuda_event, ee.cuda_event)
+    kern_ms, kern_bytes = [], []
+    with torch.cuda.stream(stream):
+        for _ in range(args.profile_passes):
+            for li, (layer, (x, lg, out)) in enumerate(zip(layers, inputs)):
+                if scrub is not None:
+                    scrub.zero_()
+                layer.run(x, lg, out, stream=stream)
+                evs[li][1].synchronize()
+                kern_ms.append(evs[li][0].elapsed_time(evs[li][1]))
+                kern_bytes.append(weight_bytes[li])
+    for layer in layers:
+        B.moe_decode_profile_events(layer.handle, None, None)
+    kern_avg_ms = float(np.mean(kern_ms))
+    achieved = float(np.mean(kern_bytes)) / (kern_avg_ms * 1e-3) / 1e9
+    log(f"expert kernel avg {kern_avg_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    # ---- CPU oracle on a bounded sample: layer 0, all m tokens
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rid, _ = oracle.route(gen.make_logits(w, 0, m), w.top_k)
+        experts = np.unique(rid)
+        d = gen.make_layer(w, 0, experts=experts)
+        d["workload"] = w
+        case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
+        L = oracle.Layer.from_case(case)
+        t = time.perf_counter()
+        r = L.run(case["x"], case["logits"])
+        cpu_s = time.perf_counter() - t
+        ref = r["out"]
+        got = inputs[0][2].cpu().numpy().astype(np.float64)
+        rel = float(np.max(np.max(np.abs(got - ref), 1) / np.max(np.abs(ref), 1)))
+        cpu = {"value": weight_bytes[0] / cpu_s / 1e9, "unit": "GB/s", "cores": int(r["threads"]),
+               "kind": "oracle",
+               "sample": f"layer 0 of {w.name}, all {m} tokens ({m * w.top_k} expert FFNs, "
+                         f"{len(experts)} hit experts), {cpu_s:.1f} s",
+               "rel_err_vs_gpu": rel}
+        log(f"oracle {cpu_s:.1f} s on {r['threads']} threads -> {cpu['value']:.4f} GB/s; "
+            f"GPU vs oracle rel {rel:.2e}")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: {n_layers} x MoE layer (E={w.num_experts}, top-{w.top_k}, "
+                         f"hidden {w.hidden}, inter {w.inter}, {w.fmt} {w.bits_mix}, "
+                         f"{w.router} routing), m={m}, "
+                         + ("one HIP graph" if stacked else "1 GiB cache scrub per launch")),
+            "layers": n_layers,
+            "m": m,
+            "us_per_launch": round(us_per_layer, 2),
+            "weight_bytes_per_step": int(step_bytes),
+            "hit_experts_per_layer": float(np.mean(hit)),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "expert_kernel",
+            "kernel_us_per_launch": round(kern_avg_ms * 1e3, 2),
+            "bytes_per_launch": int(np.mean(kern_bytes)),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    for layer in layers:
+        layer.close()
+
+
+if __name__ == "__main__":
+    main()

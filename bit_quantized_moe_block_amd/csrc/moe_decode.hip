@@ -1,0 +1,371 @@
+// Host side of the C ABI declared in include/moe_decode.h.
+//
+// create() validates the configuration before touching the HIP runtime,
+// copies the descriptor table to the device, allocates one scratch block per
+// handle and sizes the persistent expert grid per token count from the
+// occupancy calculator (no autotuning: page "lna-lab/README.md", "The three
+// traps", item 2 -- a tuner running under graph capture broke decode).
+// run() only enqueues kernels, so it can be captured into a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moe_decode.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+struct moe_decode_s {
+    Params p{};
+    int device = 0;
+    int cu_count = 0;
+    int max_tokens = 0;
+    void *scratch = nullptr;
+    size_t scratch_bytes = 0;
+    DevTensor *dev_tensors = nullptr;
+    std::vector<int> grid;       // [m] persistent grid of the expert kernel
+    std::vector<int> bpc;        // [m] resident blocks per CU
+    std::vector<size_t> lds;     // [m] dynamic LDS bytes
+    bool bound = false;
+    hipStream_t stream = nullptr;
+    bool ran = false;
+    int last_m = 0;
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+};
+
+static thread_local std::string g_err;
+
+static moe_status fail(moe_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+static moe_status fail(moe_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define HIP_TRY(call)                                                                       \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail(MOE_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_));          \
+    } while (0)
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Columns per split: 128 x the largest divisor d of C/128 with d <= 8.
+static int split_cols(int C)
+{
+    int g = C / 128, best = 1;
+    for (int d = 1; d <= 8; ++d)
+        if (g % d == 0)
+            best = d;
+    return 128 * best;
+}
+
+static moe_status validate(const moe_decode_config *c)
+{
+    if (!c)
+        return fail(MOE_E_INVALID, "cfg is NULL");
+    if (c->abi_version != MOE_DECODE_ABI_VERSION)
+        return fail(MOE_E_INVALID, "abi_version %u, library is %u", c->abi_version,
+                    MOE_DECODE_ABI_VERSION);
+    if (c->format != MOE_FMT_CODEBOOK && c->format != MOE_FMT_NVFP4)
+        return fail(MOE_E_INVALID, "unknown format %d", c->format);
+    if (c->num_experts < 1)
+        return fail(MOE_E_INVALID, "num_experts %d < 1", c->num_experts);
+    if (c->num_experts > kMaxExperts)
+        return fail(MOE_E_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
+    if (c->top_k < 1 || c->top_k > c->num_experts)
+        return fail(MOE_E_INVALID, "top_k %d not in 1..num_experts", c->top_k);
+    if (c->top_k > kMaxTopK)
+        return fail(MOE_E_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
+    if (c->hidden < 256 || c->hidden % 256)
+        return fail(MOE_E_INVALID, "hidden %d is not a positive multiple of 256", c->hidden);
+    if (c->inter < 128 || c->inter % 128)
+        return fail(MOE_E_INVALID, "inter %d is not a positive multiple of 128", c->inter);
+    if (c->hidden > 16384 || c->inter > 16384)
+        return fail(MOE_E_UNSUPPORTED, "hidden/inter above 16384");
+    if (c->max_tokens < 1)
+        return fail(MOE_E_INVALID, "max_tokens %d < 1", c->max_tokens);
+    if (c->max_tokens > kMaxTokens)
+        return fail(MOE_E_UNSUPPORTED, "max_tokens %d > %d", c->max_tokens, kMaxTokens);
+    if (!c->tensors)
+        return fail(MOE_E_INVALID, "tensors is NULL");
+    const bool cb = c->format == MOE_FMT_CODEBOOK;
+    if (cb && (!c->signs_hidden || !c->signs_inter))
+        return fail(MOE_E_INVALID, "codebook format needs signs_hidden and signs_inter");
+    for (int e = 0; e < c->num_experts; ++e) {
+        const int b0 = c->tensors[3 * e].bits;
+        for (int p = 0; p < 3; ++p) {
+            const moe_tensor_desc &t = c->tensors[3 * e + p];
+            if (!t.codes || !t.scales)
+                return fail(MOE_E_INVALID, "expert %d projection %d: NULL codes or scales", e, p);
+            if (t.bits != b0)
+                return fail(MOE_E_INVALID, "expert %d: projections have different bits", e);
+            if (cb) {
+                if (t.bits != 2 && t.bits != 3)
+                    return fail(MOE_E_INVALID, "expert %d projection %d: bits %d not 2 or 3", e, p,
+                                t.bits);
+                if (!t.lut)
+                    return fail(MOE_E_INVALID, "expert %d projection %d: NULL lut", e, p);
+                if (!aligned(t.codes, 16) || !aligned(t.scales, 2) || !aligned(t.lut, 4))
+                    return fail(MOE_E_INVALID, "expert %d projection %d: misaligned pointer", e, p);
+            } else {
+                if (t.bits != 4)
+                    return fail(MOE_E_INVALID, "expert %d projection %d: NVFP4 needs bits 4", e, p);
+                if (t.lut)
+                    return fail(MOE_E_INVALID, "expert %d projection %d: NVFP4 takes no lut", e, p);
+                if (!aligned(t.codes, 16))
+                    return fail(MOE_E_INVALID, "expert %d projection %d: misaligned codes", e, p);
+            }
+        }
+    }
+    if (!cb)
+        return fail(MOE_E_UNSUPPORTED, "NVFP4 experts are not supported by this build yet");
+    return MOE_OK;
+}
+
+extern "C" const char *moe_decode_last_error(void) { return g_err.c_str(); }
+
+extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out)
+{
+    if (!out)
+        return fail(MOE_E_INVALID, "out is NULL");
+    *out = nullptr;
+    moe_status st = validate(cfg);
+    if (st != MOE_OK)
+        return st;
+
+    moe_decode_s *h = new moe_decode_s();
+    Params &p = h->p;
+    p.format = cfg->format;
+    p.E = cfg->num_experts;
+    p.k = cfg->top_k;
+    p.H = cfg->hidden;
+    p.I = cfg->inter;
+    p.max_tokens = cfg->max_tokens;
+    p.kc1 = split_cols(p.H);
+    p.ks1 = p.H / p.kc1;
+    p.kc2 = split_cols(p.I);
+    p.ks2 = p.I / p.kc2;
+    p.n_rb1 = p.I / 128;
+    p.n_rb2 = p.H / 256;
+    p.pair_cap = p.max_tokens * p.k;
+    p.spin_limit = 20u * 1000u * 1000u;
+    p.signs_h = cfg->signs_hidden;
+    p.signs_i = cfg->signs_inter;
+    h->max_tokens = cfg->max_tokens;
+
+    auto cleanup = [&](moe_status s) {
+        if (h->scratch)
+            (void)hipFree(h->scratch);
+        delete h;
+        return s;
+    };
+    hipError_t err = hipGetDevice(&h->device);
+    if (err != hipSuccess)
+        return cleanup(fail(MOE_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(err)));
+    hipDeviceProp_t prop;
+    err = hipGetDeviceProperties(&prop, h->device);
+    if (err != hipSuccess)
+        return cleanup(fail(MOE_E_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(err)));
+    h->cu_count = prop.multiProcessorCount;
+
+    // Scratch layout (256-byte aligned pieces).
+    const size_t E = p.E, PC = p.pair_cap, H = p.H, I = p.I, M = p.max_tokens;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~size_t(255);
+        return o;
+    };
+    const size_t o_tensors = take(sizeof(DevTensor) * E * 3);
+    const size_t o_ids = take(4 * PC), o_wts = take(4 * PC), o_counts = take(4 * E),
+                 o_offsets = take(4 * (E + 1)), o_rows = take(4 * PC), o_pos = take(4 * PC);
+    const size_t o_plan = take(sizeof(Plan));
+    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(4 * E * p.n_rb1),
+                 o_hready = take(4 * E);
+    const size_t ctr_end = off;
+    const size_t o_xr = take(2 * M * H), o_gu = take(4 * (size_t)p.ks1 * PC * 2 * I),
+                 o_hr = take(2 * PC * I), o_y = take(4 * (size_t)p.ks2 * PC * H);
+    h->scratch_bytes = off;
+    err = hipMalloc(&h->scratch, off);
+    if (err != hipSuccess)
+        return cleanup(fail(MOE_E_NOMEM, "hipMalloc(%zu) failed: %s", off, hipGetErrorString(err)));
+    char *base = (char *)h->scratch;
+    h->dev_tensors = (DevTensor *)(base + o_tensors);
+    p.tensors = h->dev_tensors;
+    p.ids = (int32_t *)(base + o_ids);
+    p.wts = (float *)(base + o_wts);
+    p.counts = (int32_t *)(base + o_counts);
+    p.offsets = (int32_t *)(base + o_offsets);
+    p.rows = (int32_t *)(base + o_rows);
+    p.pos = (int32_t *)(base + o_pos);
+    p.plan = (Plan *)(base + o_plan);
+    p.ctr = (Counters *)(base + o_ctr);
+    p.rb_done = (uint32_t *)(base + o_rbdone);
+    p.h_ready = (uint32_t *)(base + o_hready);
+    p.xr = (_Float16 *)(base + o_xr);
+    p.gu_part = (float *)(base + o_gu);
+    p.hr = (_Float16 *)(base + o_hr);
+    p.y_part = (float *)(base + o_y);
+
+    std::vector<DevTensor> tab(E * 3);
+    for (size_t i = 0; i < E * 3; ++i) {
+        const moe_tensor_desc &t = cfg->tensors[i];
+        tab[i] = DevTensor{t.codes, t.scales, (const uint16_t *)t.lut, t.tensor_scale, t.bits};
+    }
+    err = hipMemcpy(h->dev_tensors, tab.data(), sizeof(DevTensor) * E * 3, hipMemcpyHostToDevice);
+    if (err == hipSuccess)
+        err = hipMemset(base + o_ids, 0, ctr_end - o_ids);
+    if (err == hipSuccess)
+        err = hipDeviceSynchronize();
+    if (err != hipSuccess)
+        return cleanup(fail(MOE_E_HIP, "scratch initialisation failed: %s", hipGetErrorString(err)));
+
+    // Persistent grid per token count: resident blocks per CU x CUs.
+    const int kc = std::max(p.kc1, p.kc2);
+    h->grid.assign(M + 1, 0);
+    h->bpc.assign(M + 1, 0);
+    h->lds.assign(M + 1, 0);
+    for (int m = 1; m <= (int)M; ++m) {
+        const size_t lds = (size_t)m * (kc + kLdsPadHalves) * sizeof(_Float16);
+        int bpc = 0;
+        err = expert_occupancy(&bpc, lds);
+        if (err != hipSuccess || bpc < 1)
+            return cleanup(fail(MOE_E_UNSUPPORTED, "expert kernel cannot be resident with %zu B LDS",
+                                lds));
+        h->bpc[m] = bpc;
+        h->lds[m] = lds;
+        h->grid[m] = bpc * h->cu_count;
+    }
+    if (getenv("MOE_DECODE_LOG"))
+        fprintf(stderr,
+                "[moe_decode] ACTIVE: gfx950 routed-experts decode, E=%d k=%d H=%d I=%d "
+                "max_tokens=%d, %d CUs, grid(max)=%d, scratch=%zu B\n",
+                p.E, p.k, p.H, p.I, p.max_tokens, h->cu_count, h->grid[M], h->scratch_bytes);
+    *out = h;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits,
+                                     float *out, int32_t m, void *hip_stream)
+{
+    if (!h)
+        return fail(MOE_E_INVALID, "handle is NULL");
+    if (m < 0 || m > h->max_tokens)
+        return fail(MOE_E_INVALID, "m = %d not in 0..max_tokens (%d)", m, h->max_tokens);
+    if (m == 0)
+        return MOE_OK;
+    if (!x_bf16 || !logits || !out)
+        return fail(MOE_E_INVALID, "NULL x, logits or out");
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (h->bound && s != h->stream)
+        return fail(MOE_E_STREAM, "handle is bound to another stream");
+    h->bound = true;
+    h->stream = s;
+    HIP_TRY(launch_route(h->p, (const uint16_t *)x_bf16, logits, m, s));
+    if (h->ev_begin)
+        HIP_TRY(hipEventRecord(h->ev_begin, s));
+    HIP_TRY(launch_expert(h->p, h->grid[m], h->lds[m], s));
+    if (h->ev_end)
+        HIP_TRY(hipEventRecord(h->ev_end, s));
+    HIP_TRY(launch_combine(h->p, out, m, s));
+    h->ran = true;
+    h->last_m = m;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_destroy(moe_decode_t h)
+{
+    if (!h)
+        return MOE_OK;
+    hipError_t err = hipSuccess;
+    if (h->scratch) {
+        if (h->bound)
+            err = hipStreamSynchronize(h->stream);
+        hipError_t e2 = hipFree(h->scratch);
+        if (err == hipSuccess)
+            err = e2;
+    }
+    delete h;
+    if (err != hipSuccess)
+        return fail(MOE_E_HIP, "destroy: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_buf, size_t bytes)
+{
+    if (!h)
+        return fail(MOE_E_INVALID, "handle is NULL");
+    if (!host_buf)
+        return fail(MOE_E_INVALID, "host_buf is NULL");
+    const Params &p = h->p;
+    if (what == MOE_Q_INFO) {
+        if (bytes < sizeof(moe_decode_info))
+            return fail(MOE_E_INVALID, "buffer too small for moe_decode_info");
+        moe_decode_info info{};
+        info.cu_count = h->cu_count;
+        info.grid_blocks = h->grid[h->max_tokens];
+        info.blocks_per_cu = h->bpc[h->max_tokens];
+        info.k_split_gate_up = p.ks1;
+        info.k_split_down = p.ks2;
+        info.scratch_bytes = (int64_t)h->scratch_bytes;
+        memcpy(host_buf, &info, sizeof info);
+        return MOE_OK;
+    }
+    if (what != MOE_Q_ROUTING && what != MOE_Q_BUCKETS && what != MOE_Q_STATS)
+        return fail(MOE_E_INVALID, "unknown query item %d", what);
+    if (!h->ran)
+        return fail(MOE_E_INVALID, "no run yet");
+    const int m = h->last_m, np = m * p.k;
+    size_t need = what == MOE_Q_ROUTING  ? (size_t)np * 8
+                  : what == MOE_Q_BUCKETS ? (size_t)(2 * p.E + 1 + np) * 4
+                                          : sizeof(moe_decode_stats);
+    if (bytes < need)
+        return fail(MOE_E_INVALID, "buffer too small (%zu < %zu)", bytes, need);
+    HIP_TRY(hipStreamSynchronize(h->stream));
+    char *dst = (char *)host_buf;
+    if (what == MOE_Q_ROUTING) {
+        HIP_TRY(hipMemcpy(dst, p.ids, 4 * np, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst + 4 * np, p.wts, 4 * np, hipMemcpyDeviceToHost));
+    } else if (what == MOE_Q_BUCKETS) {
+        HIP_TRY(hipMemcpy(dst, p.counts, 4 * p.E, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst + 4 * p.E, p.offsets, 4 * (p.E + 1), hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst + 4 * (2 * p.E + 1), p.rows, 4 * np, hipMemcpyDeviceToHost));
+    } else {
+        Plan plan;
+        Counters c;
+        HIP_TRY(hipMemcpy(&plan, p.plan, sizeof plan, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(&c, p.ctr, sizeof c, hipMemcpyDeviceToHost));
+        moe_decode_stats st{};
+        st.m = plan.m;
+        st.hit_experts = plan.n_hit;
+        st.items = plan.n_items;
+        st.items_done = (int32_t)c.items_done;
+        st.error_word = (int32_t)c.error_word;
+        memcpy(dst, &st, sizeof st);
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_profile_events(moe_decode_t h, void *ev_begin, void *ev_end)
+{
+    if (!h)
+        return fail(MOE_E_INVALID, "handle is NULL");
+    if ((ev_begin == nullptr) != (ev_end == nullptr))
+        return fail(MOE_E_INVALID, "pass both events or neither");
+    h->ev_begin = (hipEvent_t)ev_begin;
+    h->ev_end = (hipEvent_t)ev_end;
+    return MOE_OK;
+}

@@ -1,0 +1,86 @@
+// Internal structures shared by the host side of the C ABI and the gfx950
+// kernels of the routed-experts decode step. Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kThreads = 256;       // every kernel: 4 wave64s
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxTokens = 32;      // at most two 16-row MFMA token blocks
+constexpr int kMaxPairs = kMaxTokens * kMaxTopK;
+constexpr int kLdsPadHalves = 8;    // 16 B row padding of the staged activations
+
+constexpr int kFmtCodebook = 1;
+constexpr int kFmtNvfp4 = 2;
+
+// Error bits of Counters::error_word.
+constexpr uint32_t kErrSpinLimit = 1u;
+
+// One stored expert projection on the device (copied from moe_tensor_desc).
+struct DevTensor {
+    const void *codes;
+    const void *scales;
+    const uint16_t *lut;
+    float tensor_scale;
+    int32_t bits;
+};
+
+// Routing result of one run, written by the route kernel (its last block).
+struct Plan {
+    int32_t m;
+    int32_t n_hit;         // experts with >= 1 row
+    int32_t n_items1;      // gate/up work items
+    int32_t n_items;       // all work items
+    int32_t hit_expert[kMaxExperts];  // expert id of hit expert u (ascending)
+    int32_t hit_off[kMaxExperts];     // first row of u in the bucket row list
+    int32_t hit_rows[kMaxExperts];    // R_u
+};
+
+struct Counters {
+    uint32_t route_done;   // route blocks finished (reset by the last one)
+    uint32_t ticket;       // dynamic work-item tickets handed out
+    uint32_t items_done;   // work items completed (statistics)
+    uint32_t error_word;   // kErr* bits
+    uint32_t pad[4];
+};
+
+// Everything a kernel needs, passed by value.
+struct Params {
+    int32_t format, E, k, H, I, max_tokens;
+    int32_t ks1, kc1;      // gate/up: column splits and columns per split
+    int32_t ks2, kc2;      // down: column splits and columns per split
+    int32_t n_rb1;         // I / 128 gate/up row blocks of 128 (one rotation block each)
+    int32_t n_rb2;         // H / 256 down row blocks of 256
+    int32_t pair_cap;      // max_tokens * k
+    uint32_t spin_limit;   // polls before a dependency wait gives up
+    const DevTensor *tensors;   // [E*3]
+    const int8_t *signs_h;      // [H]
+    const int8_t *signs_i;      // [I]
+    int32_t *ids;          // [pair_cap] expert of (t, j)
+    float *wts;            // [pair_cap] router weight of (t, j)
+    int32_t *counts;       // [E]
+    int32_t *offsets;      // [E+1]
+    int32_t *rows;         // [pair_cap] bucket row list, entry t*k+j
+    int32_t *pos;          // [pair_cap] bucket position of (t, j)
+    Plan *plan;
+    _Float16 *xr;          // [max_tokens][H] rotated activations (fp16)
+    float *gu_part;        // [ks1][pair_cap][2][I] gate/up partial sums
+    _Float16 *hr;          // [pair_cap][I] rotated SiLU(g)*u (fp16)
+    float *y_part;         // [ks2][pair_cap][H] down partial sums
+    Counters *ctr;
+    uint32_t *rb_done;     // [E][n_rb1] finished column splits per row block
+    uint32_t *h_ready;     // [E] finished row blocks of h per hit expert
+};
+
+// Kernel launchers (kernels.hip).
+hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits, int m,
+                        hipStream_t s);
+hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s);
+hipError_t launch_combine(const Params &p, float *out, int m, hipStream_t s);
+// Occupancy of the expert kernel for a given dynamic LDS size.
+hipError_t expert_occupancy(int *blocks_per_cu, size_t lds_bytes);
+
+}  // namespace moe

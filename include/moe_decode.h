@@ -1,0 +1,183 @@
+/*
+ * moe_decode.h -- C ABI of the routed-experts decode step of a bit-quantized
+ * mixture-of-experts layer on AMD Instinct MI355X (gfx950).
+ *
+ * One call of moe_decode_run() performs the whole step for m <= max_tokens
+ * tokens: top-k routing, per-expert row buckets, block-Hadamard rotation of
+ * the activations, the fused gate/up GEMV of every hit expert on its rows,
+ * SiLU(gate)*up, the down GEMV, and the per-token combine with the router
+ * weights in slot order. This is the routed-experts decode kernel of page
+ * "LNA-CANON.md", section "lna2 とは" (rows per expert R_e in {1,2,4,8} at
+ * m <= 24, resident expert teams with dynamic tickets and no grid-wide
+ * barrier, one scratch per device, one stream at a time, bitwise reproducible)
+ * and of page "lna-lab/README.md", section "2026-09-04 -- house kernel lna2".
+ *
+ * Conventions (all entry points):
+ *  - Device pointers are plain device addresses (e.g. torch tensor data_ptr()).
+ *    Host pointers are marked "host".
+ *  - Return value: MOE_OK or a negative moe_status. No exception crosses the
+ *    boundary. moe_decode_last_error() gives a thread-local message about the
+ *    last failing call on the calling thread.
+ *  - Argument validation happens before any HIP call, so invalid arguments are
+ *    reported the same way with or without a GPU.
+ *  - There is no fallback path: an unsupported configuration fails at create
+ *    (page "LNA-CANON.md", section "教訓": a silent fallback passes the gate).
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DECODE_ABI_VERSION 1u
+
+typedef struct moe_decode_s *moe_decode_t; /* opaque handle, owned by the library */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_INVALID = -1,     /* bad argument (null pointer, bad shape, m out of range) */
+    MOE_E_UNSUPPORTED = -2, /* valid but not supported by this build (reported at create) */
+    MOE_E_HIP = -3,         /* a HIP runtime call failed (message names it) */
+    MOE_E_NOMEM = -4,       /* device scratch allocation failed */
+    MOE_E_STREAM = -5,      /* run() on a stream other than the one the handle is bound to */
+    MOE_E_DEVICE = -6       /* a kernel reported an error (see MOE_Q_STATS.error_word) */
+} moe_status;
+
+typedef enum { MOE_FMT_CODEBOOK = 1, MOE_FMT_NVFP4 = 2 } moe_format;
+
+/*
+ * One stored expert projection (gate, up or down). All pointers are device
+ * pointers BORROWED by the handle: the memory must stay allocated and
+ * unmodified until moe_decode_destroy().
+ *
+ * Matrix W has N rows (outputs) and C columns (inputs): gate and up are
+ * inter x hidden, down is hidden x inter. It is stored as tiles of 16 rows x
+ * 128 columns, tile (rb, g) at index rb*(C/128)+g, tiles in index order; a
+ * tile has 64 slots, slot l covering row 16rb + (l mod 16) and the columns
+ * 128g + 32(l div 16) + jj, jj = 0..31, slots in order.
+ *
+ * MOE_FMT_CODEBOOK (bits = 2 or 3): stand-in for the 2/3-bit codes that the
+ * pages name but do not define (page "lna-lab/README.md", "What is in the
+ * pack"). Weights live in the rotated basis (see signs_* below).
+ *   codes  : uint32 words, bits words per slot (tile = 64*bits words). Column
+ *            jj of a slot (d = jj/16, kk = jj%16): low two code bits at word d,
+ *            bit 8(kk%4) + 2(kk/4); for bits = 3 the high bit at word 2,
+ *            bit 8(kk%4) + kk/4 + 4d. 4-byte aligned.
+ *   scales : fp16, one per (row, 128-column group), scales[tau*16 + n%16].
+ *   lut    : fp16[2^bits] codebook. W[n][c] = lut[code] * scale.
+ *   tensor_scale: ignored.
+ * MOE_FMT_NVFP4 (bits = 4): page "V100 換引擎", sections 4.0 and 7.1.
+ *   codes  : bytes, 16 per slot; column jj in byte jj/2, low nibble for even jj
+ *            (OCP e2m1). 16-byte aligned.
+ *   scales : OCP e4m3fn bytes, one per (row, 16-column block),
+ *            scales[tau*128 + (n%16)*8 + (c%128)/16].
+ *   lut    : must be NULL.
+ *   tensor_scale: fp32 host value, copied at create.
+ *   W[n][c] = e2m1(code) * e4m3(scale) * tensor_scale.
+ * The three projections of one expert must have the same bits.
+ */
+typedef struct {
+    const void *codes;
+    const void *scales;
+    const void *lut;
+    float tensor_scale;
+    int32_t bits;
+} moe_tensor_desc;
+
+typedef struct {
+    uint32_t abi_version;            /* MOE_DECODE_ABI_VERSION */
+    int32_t format;                  /* moe_format */
+    int32_t num_experts;             /* E, 1..256 */
+    int32_t top_k;                   /* k, 1..min(16, E) */
+    int32_t hidden;                  /* H, multiple of 256, <= 16384 */
+    int32_t inter;                   /* I, multiple of 128, <= 16384 */
+    int32_t max_tokens;              /* largest m passed to run(), 1..32 */
+    const moe_tensor_desc *tensors;  /* host [E*3]: expert e -> gate, up, down at 3e, 3e+1, 3e+2;
+                                        copied at create */
+    const int8_t *signs_hidden;      /* device int8 [H] of +1/-1 (codebook; NULL for NVFP4) */
+    const int8_t *signs_inter;       /* device int8 [I] of +1/-1 (codebook; NULL for NVFP4) */
+} moe_decode_config;
+
+/*
+ * Create a handle for one layer on the current HIP device. Validates the
+ * configuration, copies the descriptor table to the device, allocates the
+ * handle's scratch (routing buffers, partial sums, counters) and zeroes its
+ * counters. Errors: MOE_E_INVALID (null cfg/out/tensors/pointers, shapes not
+ * multiples, bits mismatch, wrong abi_version), MOE_E_UNSUPPORTED (sizes over
+ * the limits above), MOE_E_HIP, MOE_E_NOMEM. On error *out is set to NULL.
+ */
+moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
+
+/*
+ * Enqueue one decode step on `hip_stream` (a hipStream_t; NULL = default
+ * stream). Asynchronous: no allocation, no host synchronisation, no tuning;
+ * safe to capture into a HIP graph.
+ *   x_bf16 : device bf16 [m][hidden], row-major.
+ *   logits : device fp32 [m][num_experts], row-major; must be finite.
+ *   out    : device fp32 [m][hidden], row-major; fully overwritten.
+ *   m      : 0..max_tokens. m = 0 returns MOE_OK and enqueues nothing.
+ * The handle binds to the first stream it runs on; a different stream later
+ * returns MOE_E_STREAM (page "LNA-CANON.md", "lna2 とは": concurrent streams
+ * are forbidden; page "lna-lab/README.md", "The three traps", item 3: two
+ * streams sharing one lock buffer deadlocked). Results are bitwise identical
+ * for identical inputs. Errors: MOE_E_INVALID, MOE_E_STREAM, MOE_E_HIP
+ * (launch failure). Device faults surface at the caller's next sync.
+ */
+moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits, float *out,
+                          int32_t m, void *hip_stream);
+
+/* Free the handle's scratch and the handle. NULL is accepted. Graphs that
+ * captured runs of the handle must not be replayed afterwards. */
+moe_status moe_decode_destroy(moe_decode_t h);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char *moe_decode_last_error(void);
+
+/* Query items (moe_decode_query `what`). All synchronise the bound stream. */
+enum {
+    MOE_Q_INFO = 1,    /* moe_decode_info */
+    MOE_Q_ROUTING = 2, /* int32 ids[m*k] then fp32 weights[m*k] of the last run */
+    MOE_Q_BUCKETS = 3, /* int32 counts[E], offsets[E+1], rows[m*k] (entry t*k+j) of the last run */
+    MOE_Q_STATS = 4    /* moe_decode_stats of the last run */
+};
+
+typedef struct {
+    int32_t cu_count;        /* compute units of the device */
+    int32_t grid_blocks;     /* workgroups of the expert kernel at max_tokens */
+    int32_t blocks_per_cu;   /* resident workgroups per CU at max_tokens */
+    int32_t k_split_gate_up; /* column splits of the gate/up GEMV */
+    int32_t k_split_down;    /* column splits of the down GEMV */
+    int32_t reserved;
+    int64_t scratch_bytes;   /* device scratch owned by the handle */
+} moe_decode_info;
+
+typedef struct {
+    int32_t m;              /* tokens of the last run */
+    int32_t hit_experts;    /* experts with at least one row */
+    int32_t items;          /* work items (tickets) of the last run */
+    int32_t items_done;     /* work items the expert kernel completed */
+    int32_t error_word;     /* 0, or a bit set by a kernel (1 = spin-wait limit reached) */
+    int32_t reserved;
+} moe_decode_stats;
+
+/* Copy the requested item into host_buf (host, `bytes` long). Errors:
+ * MOE_E_INVALID (unknown item, NULL buffer, buffer too small, no run yet for
+ * ROUTING/BUCKETS/STATS), MOE_E_HIP. */
+moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_buf, size_t bytes);
+
+/*
+ * Observability: record the hipEvent_t `ev_begin` immediately before and
+ * `ev_end` immediately after the expert kernel of every subsequent run (both
+ * on the run's stream), so callers can time that kernel alone. Pass NULL,NULL
+ * to stop. The events are borrowed. Errors: MOE_E_INVALID (only one NULL).
+ */
+moe_status moe_decode_profile_events(moe_decode_t h, void *ev_begin, void *ev_end);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

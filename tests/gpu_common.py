@@ -1,0 +1,51 @@
+"""Shared helpers of the GPU tests (parity metric, device upload, cases)."""
+import numpy as np
+import torch
+
+import oracle
+from bit_quantized_moe_block_amd import DeviceLayer
+
+# Worst token of max_i |y_gpu - y_ref| / max_i |y_ref| over the H outputs.
+REL_TOL = 2e-3
+WEIGHT_TOL = 1e-6
+
+
+def rel_err(out_gpu, out_ref, tokens=None):
+    g = np.asarray(out_gpu, np.float64)
+    r = np.asarray(out_ref, np.float64)
+    if tokens is not None:
+        g, r = g[tokens], r[tokens]
+    num = np.max(np.abs(g - r), axis=1)
+    den = np.max(np.abs(r), axis=1)
+    return float(np.max(num / np.where(den > 0, den, 1.0)))
+
+
+def to_dev(case, m=None):
+    x = torch.from_numpy(case["x"].view(np.int16)).cuda()
+    lg = torch.from_numpy(case["logits"]).cuda()
+    out = torch.full((x.shape[0], case["workload"].hidden), float("nan"), device="cuda")
+    return x, lg, out
+
+
+def run_gpu(layer: DeviceLayer, case, stream=None):
+    x, lg, out = to_dev(case)
+    layer.run(x, lg, out, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_routing(layer, case, m):
+    ids, w = layer.routing(m)
+    rid, rw = oracle.route(case["logits"], case["workload"].top_k)
+    assert np.array_equal(ids, rid), "routing ids differ"
+    assert np.max(np.abs(w.astype(np.float64) - rw)) <= WEIGHT_TOL
+    b = layer.buckets(m)
+    rb = oracle.bucket(rid, case["workload"].num_experts)
+    assert np.array_equal(b["counts"], rb["counts"])
+    assert np.array_equal(b["offsets"], rb["offsets"])
+    k = case["workload"].top_k
+    assert np.array_equal(b["rows"], rb["rows_t"] * k + rb["rows_j"])

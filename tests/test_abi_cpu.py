@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: symbols, argument validation, error messages.
+
+Every call here fails validation before the library touches the HIP runtime,
+so nothing runs on a device. (CPU only.)
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_quantized_moe_block_amd as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*)\s*(moe_decode_\w+)\(", src,
+                                 re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(B.EXPORTED)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    assert int(re.search(r"MOE_DECODE_ABI_VERSION (\d+)u", src).group(1)) == B.MOE_DECODE_ABI_VERSION
+    for name, val in [("MOE_E_INVALID", -1), ("MOE_E_UNSUPPORTED", -2), ("MOE_E_HIP", -3),
+                      ("MOE_E_NOMEM", -4), ("MOE_E_STREAM", -5), ("MOE_E_DEVICE", -6)]:
+        assert re.search(rf"{name} = {val}", src), name
+        assert getattr(B, name) == val
+    assert C.sizeof(B.moe_tensor_desc) == 32
+    assert C.sizeof(B.moe_decode_info) == 32
+    assert C.sizeof(B.moe_decode_stats) == 24
+
+
+def make_cfg(E=4, k=2, H=256, I=128, M=4, bits=2, fmt=B.MOE_FMT_CODEBOOK, **over):
+    descs = (B.moe_tensor_desc * (3 * E))()
+    for i in range(3 * E):
+        descs[i].codes = FAKE
+        descs[i].scales = FAKE
+        descs[i].lut = FAKE if fmt == B.MOE_FMT_CODEBOOK else None
+        descs[i].bits = bits
+    cfg = B.moe_decode_config(B.MOE_DECODE_ABI_VERSION, fmt, E, k, H, I, M,
+                              C.cast(descs, C.POINTER(B.moe_tensor_desc)), FAKE, FAKE)
+    for key, v in over.items():
+        setattr(cfg, key, v)
+    cfg._keep = descs
+    return cfg
+
+
+def create_status(cfg):
+    h = C.c_void_p()
+    st = B.lib().moe_decode_create(C.byref(cfg) if cfg is not None else None, C.byref(h))
+    assert h.value is None
+    return st, B.moe_decode_last_error()
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(abi_version=7), B.MOE_E_INVALID, "abi_version"),
+    (dict(format=9), B.MOE_E_INVALID, "format"),
+    (dict(num_experts=0), B.MOE_E_INVALID, "num_experts"),
+    (dict(top_k=0), B.MOE_E_INVALID, "top_k"),
+    (dict(top_k=5), B.MOE_E_INVALID, "top_k"),
+    (dict(hidden=384), B.MOE_E_INVALID, "hidden"),
+    (dict(inter=100), B.MOE_E_INVALID, "inter"),
+    (dict(hidden=32768), B.MOE_E_UNSUPPORTED, "16384"),
+    (dict(max_tokens=0), B.MOE_E_INVALID, "max_tokens"),
+    (dict(max_tokens=33), B.MOE_E_UNSUPPORTED, "max_tokens"),
+    (dict(signs_hidden=None), B.MOE_E_INVALID, "signs"),
+])
+def test_create_rejects_bad_config(over, status, msg):
+    st, err = create_status(make_cfg(**over))
+    assert st == status and msg in err
+
+
+def test_create_rejects_too_many_experts_and_topk():
+    assert create_status(make_cfg(E=300, k=2))[0] == B.MOE_E_UNSUPPORTED
+    assert create_status(make_cfg(E=32, k=17))[0] == B.MOE_E_UNSUPPORTED
+
+
+def test_create_rejects_bad_tensors():
+    cfg = make_cfg(bits=4)
+    assert create_status(cfg)[0] == B.MOE_E_INVALID
+    cfg = make_cfg()
+    cfg._keep[4].bits = 3           # expert 1 up differs from its gate
+    st, err = create_status(cfg)
+    assert st == B.MOE_E_INVALID and "different bits" in err
+    cfg = make_cfg()
+    cfg._keep[2].codes = None
+    assert create_status(cfg)[0] == B.MOE_E_INVALID
+    cfg = make_cfg()
+    cfg._keep[0].lut = None
+    assert "lut" in create_status(cfg)[1]
+    cfg = make_cfg()
+    cfg._keep[0].codes = FAKE + 4    # codes must be 16-byte aligned
+    assert "misaligned" in create_status(cfg)[1]
+    cfg = make_cfg(fmt=B.MOE_FMT_NVFP4, bits=4)
+    cfg._keep[0].lut = FAKE
+    assert "no lut" in create_status(cfg)[1]
+    cfg = make_cfg()
+    cfg.tensors = None
+    assert create_status(cfg)[0] == B.MOE_E_INVALID
+
+
+def test_null_arguments():
+    L = B.lib()
+    h = C.c_void_p()
+    assert L.moe_decode_create(None, C.byref(h)) == B.MOE_E_INVALID
+    cfg = make_cfg()
+    assert L.moe_decode_create(C.byref(cfg), None) == B.MOE_E_INVALID
+    assert L.moe_decode_run(None, FAKE, FAKE, FAKE, 1, None) == B.MOE_E_INVALID
+    assert "handle" in B.moe_decode_last_error()
+    assert L.moe_decode_destroy(None) == B.MOE_OK
+    buf = (C.c_char * 64)()
+    assert L.moe_decode_query(None, B.MOE_Q_INFO, buf, 64) == B.MOE_E_INVALID
+    assert L.moe_decode_profile_events(None, None, None) == B.MOE_E_INVALID
+
+
+def test_error_message_is_thread_local():
+    import threading
+    create_status(make_cfg(num_experts=0))
+    seen = {}
+
+    def other():
+        seen["msg"] = B.moe_decode_last_error()
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "num_experts" in B.moe_decode_last_error()
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(B.MoeDecodeError) as ei:
+        B.moe_decode_create(make_cfg(top_k=0))
+    assert ei.value.status == B.MOE_E_INVALID
+
+
+def test_binding_is_marshalling_only():
+    # The product path must not reach the CPU oracle or any fallback.
+    pkg = os.path.join(ROOT, "bit_quantized_moe_block_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert "oracle" not in src.replace("oracle/", ""), f
+            assert "import oracle" not in src

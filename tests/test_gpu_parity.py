@@ -1,0 +1,217 @@
+"""GPU path vs the CPU oracle through the C ABI (needs an MI355X).
+
+Sizes the oracle finishes in seconds cover several tiles and ragged tails;
+the full-size workloads are checked on sampled tokens (every expert FFN of
+those tokens, every output element) plus exact routing for all tokens.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_moe_block_amd import DeviceLayer
+from moe_synth import WORKLOADS, gen, small_workload
+from tests.gpu_common import REL_TOL, check_routing, rel_err, run_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def parity(case, tokens=None, max_tokens=None):
+    w = case["workload"]
+    m = case["x"].shape[0]
+    say(f"[parity] {w.name} E={w.num_experts} k={w.top_k} H={w.hidden} I={w.inter} m={m}")
+    layer = DeviceLayer.from_case(case, max_tokens=max_tokens or m)
+    try:
+        out = run_gpu(layer, case)
+        check_routing(layer, case, m)
+        st = layer.stats()
+        assert st.error_word == 0 and st.items_done == st.items
+        ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+        err = rel_err(out, ref["out"], tokens)
+        say(f"    rel={err:.3e}")
+        assert err <= REL_TOL
+        return layer, out
+    finally:
+        layer.close()
+
+
+def test_tiny():
+    parity(gen.make_case(WORKLOADS["tiny"], 1))
+
+
+GRID = []
+_rng = np.random.default_rng(12345)
+for i in range(24):
+    E = int(_rng.choice([8, 16, 32]))
+    k = int(_rng.choice([1, 2, 3, 4]))
+    H = int(_rng.choice([256, 512, 1024]))
+    I = int(_rng.choice([128, 256, 384]))
+    m = int(_rng.integers(1, 25))
+    mix = str(_rng.choice(["all2", "alternate", "all3"]))
+    GRID.append((small_workload(f"grid{i}", E, k, H, I, bits_mix=mix, config_id=1000 + i), m))
+
+
+@pytest.mark.parametrize("w,m", GRID, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_random_grid(w, m):
+    parity(gen.make_case(w, m))
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_rank_share(m):
+    parity(gen.make_case(WORKLOADS["rank_share"], m))
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    w = WORKLOADS["full_layer"]
+    d = gen.make_layer(w, 0)
+    d["workload"] = w
+    layer = DeviceLayer.from_case(d, max_tokens=w.max_tokens)
+    yield d, layer
+    layer.close()
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 24])
+def test_full_layer_sampled(full_layer, m):
+    d, layer = full_layer
+    w = d["workload"]
+    case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
+    say(f"[parity] full_layer m={m}")
+    out = run_gpu(layer, case)
+    check_routing(layer, case, m)
+    st = layer.stats()
+    assert st.error_word == 0 and st.items_done == st.items
+    tokens = sorted(set([0, m - 1, m // 2]))
+    ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+    err = rel_err(out, ref["out"], tokens)
+    say(f"    rel={err:.3e} hit={st.hit_experts} items={st.items}")
+    assert err <= REL_TOL
+    assert np.all(np.isfinite(out))
+
+
+def test_bitwise_repeatable_and_graph_replay():
+    w = small_workload("rep", 16, 4, 1024, 256, bits_mix="alternate", config_id=301)
+    case = gen.make_case(w, 24)
+    say("[bitwise] 10 direct runs + graph replays")
+    s = torch.cuda.Stream()
+    layer = DeviceLayer.from_case(case, max_tokens=24)
+    try:
+        x, lg, out = to_dev(case)
+        outs = []
+        with torch.cuda.stream(s):
+            for _ in range(10):
+                out.fill_(float("nan"))
+                layer.run(x, lg, out, stream=s)
+                s.synchronize()
+                outs.append(out.clone())
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+        g = torch.cuda.CUDAGraph()
+        out_g = torch.full_like(out, float("nan"))
+        with torch.cuda.graph(g, stream=s):
+            layer.run(x, lg, out_g, stream=s)
+        for rep in range(5):
+            out_g.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_g.view(torch.int32), outs[0].view(torch.int32)), rep
+            with torch.cuda.stream(s):       # eager work between replays
+                layer.run(x, lg, out, stream=s)
+            s.synchronize()
+            assert torch.equal(out.view(torch.int32), outs[0].view(torch.int32))
+        # a fresh handle on the same inputs gives the same bytes
+        layer2 = DeviceLayer.from_case(case, max_tokens=24)
+        out2 = torch.full_like(out, float("nan"))
+        layer2.run(x, lg, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.int32), outs[0].view(torch.int32))
+        layer2.close()
+    finally:
+        layer.close()
+
+
+def test_zero_input_exact_zero():
+    w = small_workload("zero", 8, 2, 512, 256, bits_mix="alternate", config_id=302)
+    case = gen.make_case(w, 5)
+    case["x"] = np.zeros_like(case["x"])
+    layer = DeviceLayer.from_case(case)
+    try:
+        out = run_gpu(layer, case)
+        assert np.all(out == 0.0)
+    finally:
+        layer.close()
+
+
+def test_all_tokens_same_experts_hot_path():
+    # Every token routes to the same k experts: R_e = m = 24 (two MFMA token
+    # blocks, rows beyond 16), the largest bucket the path admits at m = 24.
+    w = small_workload("hot", 32, 4, 1024, 384, bits_mix="alternate", config_id=303)
+    case = gen.make_case(w, 24)
+    lg = case["logits"].copy()
+    lg[:, [3, 17, 8, 30]] += 50.0
+    case["logits"] = lg
+    layer, _ = parity(case)
+    b = oracle.bucket(oracle.route(lg, 4)[0], 32)
+    assert sorted(np.nonzero(b["counts"])[0].tolist()) == [3, 8, 17, 30]
+
+
+def test_tied_logits():
+    w = small_workload("ties", 16, 4, 256, 128, bits_mix="all3", config_id=304)
+    case = gen.make_case(w, 6)
+    lg = case["logits"].copy()
+    lg[:, 5] = lg[:, 2]
+    lg[0, :] = 0.5
+    lg[1, :] = -0.0
+    lg[1, 9] = 0.0
+    case["logits"] = lg
+    parity(case)
+
+
+def test_m_zero_and_range_errors():
+    import bit_quantized_moe_block_amd as B
+    w = small_workload("mz", 8, 2, 256, 128, config_id=305)
+    case = gen.make_case(w, 2)
+    layer = DeviceLayer.from_case(case, max_tokens=2)
+    try:
+        x, lg, out = to_dev(case)
+        out.fill_(7.0)
+        layer.run(x, lg, out, m=0)
+        torch.cuda.synchronize()
+        assert torch.all(out == 7.0)
+        with pytest.raises(B.MoeDecodeError) as ei:
+            layer.run(x, lg, out, m=3)
+        assert ei.value.status == B.MOE_E_INVALID
+        layer.run(x, lg, out)                # first real run binds the current stream
+        torch.cuda.synchronize()
+        other = torch.cuda.Stream()
+        with pytest.raises(B.MoeDecodeError) as ei:
+            layer.run(x, lg, out, stream=other)
+        assert ei.value.status == B.MOE_E_STREAM
+    finally:
+        layer.close()
+
+
+def test_tokens_fewer_than_max_tokens():
+    # A handle sized for 24 tokens run with m = 3, then m = 11, then m = 3 again.
+    w = small_workload("var", 16, 3, 512, 256, bits_mix="alternate", config_id=306)
+    d = gen.make_layer(w, 0)
+    d["workload"] = w
+    layer = DeviceLayer.from_case(d, max_tokens=24)
+    try:
+        for m in (3, 11, 3):
+            case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
+            out = run_gpu(layer, case)
+            check_routing(layer, case, m)
+            ref = oracle.Layer.from_case(case).run(case["x"], case["logits"])
+            assert rel_err(out, ref["out"]) <= REL_TOL
+    finally:
+        layer.close()
