@@ -67,14 +67,15 @@ typedef enum { MOE_FMT_CODEBOOK = 1, MOE_FMT_NVFP4 = 2 } moe_format;
  *            jj of a slot (d = jj/16, kk = jj%16): low two code bits at word d,
  *            bit 8(kk%4) + 2(kk/4); for bits = 3 the high bit at word 2,
  *            bit 8(kk%4) + kk/4 + 4d. 4-byte aligned.
- *   scales : fp16, one per (row, 128-column group), scales[tau*16 + n%16].
+ *   scales : fp16, one per (row, 128-column group), row-major:
+ *            scales[n*(C/128) + c/128]. 16-byte aligned.
  *   lut    : fp16[2^bits] codebook. W[n][c] = lut[code] * scale.
  *   tensor_scale: ignored.
  * MOE_FMT_NVFP4 (bits = 4): page "V100 換引擎", sections 4.0 and 7.1.
  *   codes  : bytes, 16 per slot; column jj in byte jj/2, low nibble for even jj
  *            (OCP e2m1). 16-byte aligned.
- *   scales : OCP e4m3fn bytes, one per (row, 16-column block),
- *            scales[tau*128 + (n%16)*8 + (c%128)/16].
+ *   scales : OCP e4m3fn bytes, one per (row, 16-column block), row-major:
+ *            scales[n*(C/16) + c/16].
  *   lut    : must be NULL.
  *   tensor_scale: fp32 host value, copied at create.
  *   W[n][c] = e2m1(code) * e4m3(scale) * tensor_scale.

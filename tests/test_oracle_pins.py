@@ -141,9 +141,8 @@ def test_codebook_roundtrip_exact_weights(bits):
                            - lut.astype(np.float64)[None, None, :]), axis=-1)
     assert np.array_equal(enc, codes)
     words = brute.pack_codebook(enc, bits)
-    tile_scales = sc.reshape(N // 16, 16, C // 128).transpose(0, 2, 1).reshape(-1)
     L = oracle.Layer("codebook", 1, 1, C, N, [bits],
-                     {(0, 0): dict(codes=words, scales=tile_scales, lut=lut)})
+                     {(0, 0): dict(codes=words, scales=sc.reshape(-1), lut=lut)})
     assert np.array_equal(L.dequant(0, 0), W)
 
 
