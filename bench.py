@@ -43,6 +43,31 @@ def parse():
     return ap.parse_args()
 
 
+class HipEvent:
+    """A raw hipEvent_t (timing enabled) for events recorded inside the library."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._c = ctypes
+        ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.ptr = ev.value
+
+    def elapsed_ms(self, end):
+        ms = self._c.c_float()
+        h = HipEvent._hip
+        if h.hipEventSynchronize(self._c.c_void_p(end.ptr)) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if h.hipEventElapsedTime(self._c.byref(ms), self._c.c_void_p(self.ptr),
+                                 self._c.c_void_p(end.ptr)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -164,12 +189,12 @@ def main():
     log(f"step {ms_per_step:.3f} ms (wall {wall:.3f} ms), {us_per_layer:.1f} us/layer, "
         f"{value:.0f} GB/s")
 
-    # ---- dominant kernel alone: HIP events around the expert kernel
+    # ---- dominant kernel alone: HIP events recorded by the library right
+    # before and after the expert kernel, on the stream it is launched on.
     import bit_quantized_moe_block_amd as B
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in layers]
+    evs = [(HipEvent(), HipEvent()) for _ in layers]
     for layer, (eb, ee) in zip(layers, evs):
-        B.moe_decode_profile_events(layer.handle, eb.cuda_event, ee.cuda_event)
+        B.moe_decode_profile_events(layer.handle, eb.ptr, ee.ptr)
     kern_ms, kern_bytes = [], []
     with torch.cuda.stream(stream):
         for _ in range(args.profile_passes):
@@ -177,8 +202,7 @@ def main():
                 if scrub is not None:
                     scrub.zero_()
                 layer.run(x, lg, out, stream=stream)
-                evs[li][1].synchronize()
-                kern_ms.append(evs[li][0].elapsed_time(evs[li][1]))
+                kern_ms.append(evs[li][0].elapsed_ms(evs[li][1]))
                 kern_bytes.append(weight_bytes[li])
     for layer in layers:
         B.moe_decode_profile_events(layer.handle, None, None)

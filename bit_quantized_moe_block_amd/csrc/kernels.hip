@@ -1,21 +1,26 @@
 // gfx950 kernels of the routed-experts decode step.
 //
-// route_kernel   one block per token: top-k on the raw logits, softmax over
-//                the selected logits, block-Hadamard rotation of x (codebook)
-//                or bf16->fp16 (NVFP4). The last block to finish builds the
-//                per-expert row buckets and the work plan, and resets the
-//                expert kernel's counters (so every run and every graph
-//                replay starts clean without a memset).
+// route_kernel   1024-thread blocks. Block 0: top-k on the raw logits (one
+//                wave per token, DPP max-reductions), softmax over the
+//                selected logits, per-expert row buckets, row groups (<= 16
+//                rows each), the work plan, and a reset of the expert
+//                kernel's counters (so every run and every graph replay
+//                starts clean without a memset). Blocks 1..: one wave per
+//                (token, 128-column block) rotates x (codebook) or converts
+//                it to fp16 (NVFP4). No block waits on another.
 // expert_kernel  persistent grid pulling work-item tickets, no grid-wide
-//                barrier. Gate/up items (one hit expert, 128 rows of gate and
+//                barrier. Gate/up items (one row group, 128 rows of gate and
 //                of up, one column split) write partial sums; the last split
 //                of a 128-row block finishes SiLU(g)*u and the 128-point
 //                rotation of h. Down items (256 rows of down, one column
-//                split) wait on a per-expert counter of finished h blocks.
-//                Inner loop: codes decoded in registers through v_perm byte
-//                lookups of the per-tensor codebook, MFMA 16x16x32 f16 with
-//                the tokens as the A operand, fp32 group-scale FMAs.
-// combine_kernel out[t] = sum_j w[t][j] * y[t][j] in slot order.
+//                split) wait on a per-group counter of finished h blocks; the
+//                last down item touching a (token, 256-row block) combines
+//                that block of the token's output in slot order.
+//                Inner loop: codes decoded in registers (v_perm byte lookups
+//                of the per-tensor codebook, or hardware e2m1 conversion),
+//                MFMA 16x16x32 f16 with the tokens as the A operand, fp32
+//                group-scale FMAs; two pairs of weight groups in flight per
+//                wave (ping-pong register buffers).
 //
 // Page "LNA-CANON.md", section "lna2 とは": resident expert teams with
 // dynamic tickets and no grid-wide barrier, small-R inner loops for
@@ -28,6 +33,7 @@ namespace moe {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -41,9 +47,44 @@ __device__ __forceinline__ uint32_t atomic_load_agent(uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void atomic_store_agent(uint32_t *p, uint32_t v)
+
+// Data handed between blocks of one kernel launch (gate/up partial sums ->
+// the finishing block, h~ -> the down items, down partial sums -> the
+// combining block) moves through agent-coherent loads and stores (sc1):
+// they bypass the per-XCD L2 copies, so no L2 write-back or invalidate (what
+// a device-scope fence costs on a multi-XCD part) is needed. The producer
+// waits for its stores to be acknowledged (s_waitcnt) before a block barrier
+// and the counter increment.
+__device__ __forceinline__ void st_coherent(float *p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte agent-coherent load (buffer_load_dwordx4 ... sc1) at byte offset
+// `off` of a buffer starting at `base`.
+__device__ __forceinline__ u32x4 ld_coherent16(const void *base, uint32_t off)
+{
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7FFFFFFF, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16 /* sc1 */);
+}
+// All of this wave's memory operations acknowledged (stores included).
+__device__ __forceinline__ void wait_stores()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -74,26 +115,37 @@ __device__ __forceinline__ void wave_fwht128(float &v0, float &v1)
 // Route
 // ---------------------------------------------------------------------------
 
-// Total order for the top-k: larger logit first, equal logits -> lower id.
-// Monotone float bits in the high word, inverted id in the low word; 0 is
-// below every real key and marks "not available". -0 is folded into +0.
-__device__ __forceinline__ uint64_t route_key(float v, int e)
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+// Monotone key of a finite float: larger value <-> larger unsigned key; -0
+// is folded into +0. Key 0 is below every finite value and marks "taken".
+__device__ __forceinline__ uint32_t float_key(float v)
 {
     if (v == 0.0f)
         v = 0.0f;
-    uint32_t u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+__device__ __forceinline__ float key_float(uint32_t k)
 {
-    uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Exclusive block-wide scan of one int per thread (256 threads).
-__device__ __forceinline__ int block_excl_scan(int v, int *tmp4, int &total)
+// Maximum over the wave (DPP row shifts, then row broadcasts), as a scalar.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Exclusive block-wide scan of one int per thread (kRouteThreads threads).
+__device__ __forceinline__ int block_excl_scan(int v, int *tmp, int &total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
@@ -104,481 +156,828 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp4, int &total)
             x += y;
     }
     if (lane == 63)
-        tmp4[wave] = x;
+        tmp[wave] = x;
     __syncthreads();
     int base = 0;
-    for (int w = 0; w < wave; ++w)
-        base += tmp4[w];
-    total = tmp4[0] + tmp4[1] + tmp4[2] + tmp4[3];
+    total = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+        base += w < wave ? tmp[w] : 0;
+        total += tmp[w];
+    }
     __syncthreads();
     return base + x - v;
 }
 
-__global__ __launch_bounds__(kThreads) void route_kernel(Params p, const uint16_t *__restrict__ x,
-                                                         const float *__restrict__ logits, int m)
+__device__ void route_block(const Params &p, const float *__restrict__ logits, int m)
 {
-    __shared__ uint64_t red[4];
-    __shared__ int sel[kMaxTopK];
-    __shared__ int s_last;
     __shared__ int s_ids[kMaxPairs];
-    __shared__ int tmp4[4];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = p.E, k = p.k, H = p.H;
+    __shared__ float s_val[kMaxPairs];
+    __shared__ uint32_t s_mask[kMaxExperts];
+    __shared__ int s_off[kMaxExperts];
+    __shared__ int tmp[kRouteWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = p.E, k = p.k;
+    if (tid < kMaxExperts)
+        s_mask[tid] = 0u;
 
-    // ---- top-k by k rounds of a block-wide max over route keys
-    uint64_t key = 0;
-    if (tid < E)
-        key = route_key(logits[(size_t)t * E + tid], tid);
-    for (int j = 0; j < k; ++j) {
-        uint64_t b = key;
+    // ---- top-k: one wave per token; lane holds experts lane + 64 i. Each
+    // round takes the largest key, then the lowest expert id among equal keys.
+    for (int t = wave; t < m; t += kRouteWaves) {
+        uint32_t key[4];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            uint64_t o = shfl_xor_u64(b, off);
-            b = o > b ? o : b;
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? float_key(logits[(size_t)t * E + e]) : 0u;
         }
-        if (lane == 0)
-            red[wave] = b;
-        __syncthreads();
-        b = red[0];
-        for (int w = 1; w < 4; ++w)
-            b = red[w] > b ? red[w] : b;
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)b);
-        if (tid == 0)
-            sel[j] = e;
-        if (tid == e)
-            key = 0;
-        __syncthreads();
-    }
-    // ---- weights: softmax over the k selected logits, slot order
-    if (tid == 0) {
-        const float *l = logits + (size_t)t * E;
-        const float l0 = l[sel[0]];
-        float den = 0.0f;
-        for (int j = 0; j < k; ++j)
-            den += expf(l[sel[j]] - l0);
         for (int j = 0; j < k; ++j) {
-            p.ids[t * k + j] = sel[j];
-            p.wts[t * k + j] = expf(l[sel[j]] - l0) / den;
+            const uint32_t kmax = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+            uint32_t cand = 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = 3; i >= 0; --i)
+                if (key[i] == kmax)
+                    cand = lane + 64 * i;
+            const int e = (int)~wave_max_u32(~cand);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (e == lane + 64 * i)
+                    key[i] = 0u;
+            if (lane == 0) {
+                s_ids[t * k + j] = e;
+                s_val[t * k + j] = key_float(kmax);
+            }
+        }
+        // weights: softmax over the k selected logits, summed in slot order
+        if (lane == 0) {
+            const float l0 = s_val[t * k];
+            float den = 0.0f;
+            for (int j = 0; j < k; ++j)
+                den += expf(s_val[t * k + j] - l0);
+            for (int j = 0; j < k; ++j) {
+                p.ids[t * k + j] = s_ids[t * k + j];
+                p.wts[t * k + j] = expf(s_val[t * k + j] - l0) / den;
+            }
         }
     }
-    // ---- activations: rotated fp16 (codebook) or plain fp16 (NVFP4)
-    const uint32_t *xw = (const uint32_t *)(x + (size_t)t * H);
-    half2v *xo = (half2v *)(p.xr + (size_t)t * H);
-    if (p.format == kFmtCodebook) {
-        for (int b = wave; b < H / 128; b += 4) {
-            const int c0 = b * 128 + 2 * lane;
-            const uint32_t xx = xw[c0 / 2];
-            float v0 = bf16_to_f32(xx & 0xFFFFu) * (float)p.signs_h[c0];
-            float v1 = bf16_to_f32(xx >> 16) * (float)p.signs_h[c0 + 1];
-            wave_fwht128(v0, v1);
-            xo[c0 / 2] = half2v{(_Float16)(v0 * kInvSqrt128), (_Float16)(v1 * kInvSqrt128)};
-        }
-    } else {
-        for (int c = tid; c < H / 2; c += kThreads) {
-            const uint32_t xx = xw[c];
-            xo[c] = half2v{(_Float16)bf16_to_f32(xx & 0xFFFFu), (_Float16)bf16_to_f32(xx >> 16)};
-        }
-    }
+    __syncthreads();
 
-    // ---- the last block builds buckets and the plan
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        s_last = atomic_add_agent(&p.ctr->route_done, 1u) == (uint32_t)(m - 1);
-    __syncthreads();
-    if (!s_last)
-        return;
-    __threadfence();
+    // ---- buckets. Top-k picks distinct experts per token, so expert e's rows
+    // are the tokens of the bitmask mask[e] (t < m <= 32), ascending by t;
+    // the rank of (t, j) inside e's bucket is popcount(mask[e] below bit t).
     const int np = m * k;
-    for (int i = tid; i < np; i += kThreads)
-        s_ids[i] = p.ids[i];
+    for (int i = tid; i < np; i += kRouteThreads)
+        atomicOr(&s_mask[s_ids[i]], 1u << (i / k));
     __syncthreads();
-    int cnt = 0;
-    if (tid < E)
-        for (int i = 0; i < np; ++i)
-            cnt += s_ids[i] == tid;
-    int total;
-    const int off = block_excl_scan(cnt, tmp4, total);
-    int nhit;
-    const int u = block_excl_scan(cnt > 0 ? 1 : 0, tmp4, nhit);
+    const uint32_t mask = tid < E ? s_mask[tid] : 0u;
+    const int cnt = __popc(mask);
+    const int ng_e = (cnt + kGroupRows - 1) / kGroupRows;
+    // one scan of (rows | hit << 12 | groups << 22): sums stay below 4096 / 1024 / 1024
+    int packed_total;
+    const int packed = block_excl_scan(cnt | ((cnt > 0) << 12) | (ng_e << 22), tmp, packed_total);
+    const int off = packed & 0xFFF, gbase = packed >> 22;
+    const int total = packed_total & 0xFFF, nhit = (packed_total >> 12) & 0x3FF,
+              ngroups = packed_total >> 22;
     Plan *P = p.plan;
     if (tid < E) {
+        s_off[tid] = off;
         p.counts[tid] = cnt;
         p.offsets[tid] = off;
-        if (cnt > 0) {
-            P->hit_expert[u] = tid;
-            P->hit_off[u] = off;
-            P->hit_rows[u] = cnt;
-            int q = off;
-            for (int i = 0; i < np; ++i)
-                if (s_ids[i] == tid) {
-                    p.rows[q] = i;
-                    p.pos[i] = q;
-                    ++q;
-                }
+        for (int g = 0; g < ng_e; ++g) {
+            P->g_expert[gbase + g] = tid;
+            P->g_off[gbase + g] = off + kGroupRows * g;
+            P->g_rows[gbase + g] = min(kGroupRows, cnt - kGroupRows * g);
         }
+    }
+    __syncthreads();
+    for (int i = tid; i < np; i += kRouteThreads) {
+        const int e = s_ids[i], t = i / k;
+        const int q = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
+        p.rows[q] = i;
+        p.pos[i] = q;
     }
     if (tid == 0) {
         p.offsets[E] = total;
-        const int n1 = nhit * p.n_rb1 * p.ks1;
+        const int n1 = ngroups * p.n_rb1 * p.ks1;
         P->m = m;
         P->n_hit = nhit;
+        P->n_groups = ngroups;
         P->n_items1 = n1;
-        P->n_items = n1 + nhit * p.n_rb2 * p.ks2;
+        P->n_items = n1 + ngroups * p.n_rb2 * p.ks2;
         p.ctr->ticket = 0;
         p.ctr->items_done = 0;
         p.ctr->error_word = 0;
-        p.ctr->route_done = 0;
     }
-    for (int i = tid; i < nhit * p.n_rb1; i += kThreads)
+    for (int i = tid; i < ngroups * p.n_rb1; i += kRouteThreads)
         p.rb_done[i] = 0;
-    for (int i = tid; i < nhit; i += kThreads)
+    for (int i = tid; i < ngroups; i += kRouteThreads)
         p.h_ready[i] = 0;
+    for (int i = tid; i < m * p.n_rb2; i += kRouteThreads)
+        p.comb[i] = 0;
 }
 
-// ---------------------------------------------------------------------------
-// Expert kernel: small-R GEMV core
-// ---------------------------------------------------------------------------
-
-// Byte tables of the per-tensor codebook for v_perm lookups: lo[i] holds the
-// low bytes of entries 4i..4i+3, hi[i] the high bytes.
-template <int BITS>
-__device__ __forceinline__ void load_lut(const uint16_t *lut, uint32_t &lo0, uint32_t &lo1,
-                                         uint32_t &hi0, uint32_t &hi1)
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
+                                                              const uint16_t *__restrict__ x,
+                                                              const float *__restrict__ logits,
+                                                              int m)
 {
-    const uint32_t *L = (const uint32_t *)lut;
-    const uint32_t d0 = L[0], d1 = L[1];
-    lo0 = __builtin_amdgcn_perm(d1, d0, 0x06040200u);
-    hi0 = __builtin_amdgcn_perm(d1, d0, 0x07050301u);
-    lo1 = hi1 = 0;
-    if constexpr (BITS == 3) {
-        const uint32_t d2 = L[2], d3 = L[3];
-        lo1 = __builtin_amdgcn_perm(d3, d2, 0x06040200u);
-        hi1 = __builtin_amdgcn_perm(d3, d2, 0x07050301u);
+    if (blockIdx.x == 0) {
+        route_block(p, logits, m);
+        return;
     }
+    // one wave per (token, 128-column block) of the activations
+    const int lane = threadIdx.x & 63;
+    const int task = (blockIdx.x - 1) * kRouteWaves + (threadIdx.x >> 6);
+    const int nb = p.H / 128;
+    if (task >= m * nb)
+        return;
+    const int t = task / nb, c0 = (task - t * nb) * 128 + 2 * lane;
+    const uint32_t xx = *(const uint32_t *)(x + (size_t)t * p.H + c0);
+    float v0 = bf16_to_f32(xx & 0xFFFFu), v1 = bf16_to_f32(xx >> 16);
+    if (p.format == kFmtCodebook) {
+        v0 *= (float)p.signs_h[c0];
+        v1 *= (float)p.signs_h[c0 + 1];
+        wave_fwht128(v0, v1);
+        v0 *= kInvSqrt128;
+        v1 *= kInvSqrt128;
+    }
+    *(half2v *)(p.xr + (size_t)t * p.H + c0) = half2v{(_Float16)v0, (_Float16)v1};
 }
 
-// Decode one slot (32 codes of one row) into 16 packed fp16 pairs in natural
-// column order: pair i holds columns 2i, 2i+1 of the slot. For word d and
-// shift s, byte b of t is the code of column 16d + 4s + b; two v_perm
-// lookups give its low and high bytes, two more interleave them.
-template <int BITS>
-__device__ __forceinline__ void decode_slot(const uint32_t (&w)[BITS], uint32_t lo0, uint32_t lo1,
-                                            uint32_t hi0, uint32_t hi1, uint32_t (&out)[16])
+// ---------------------------------------------------------------------------
+// Expert kernel: the per-wave small-R GEMV core
+// ---------------------------------------------------------------------------
+
+#define GLOBAL __attribute__((address_space(1)))
+typedef const uint32_t GLOBAL *gu32p;
+typedef const uint16_t GLOBAL *gu16p;
+typedef const uint8_t GLOBAL *gu8p;
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Row blocks (16 rows each) one wave computes; waves per expert-kernel block.
+constexpr int kWaveRB = 2;
+constexpr int kExpertThreads = 512;
+constexpr int kExpertWaves = kExpertThreads / 64;
+
+// Slot words held per tile: codebook up to 3 (2-bit tensors use 2), NVFP4 4.
+template <int CLASS>
+struct Slot {
+    static constexpr int W = CLASS == kFmtCodebook ? 3 : 4;
+};
+
+// Byte tables of the per-tensor codebook for v_perm lookups: tab[0] / tab[1]
+// hold the low bytes of entries 0..3 / 4..7, tab[2] / tab[3] the high bytes.
+// `raw` holds the codebook as stored (fp16 entries, little endian); a 2-bit
+// codebook leaves raw[2], raw[3] zero.
+__device__ __forceinline__ void lut_tables(const u32x4 raw, uint32_t (&tab)[4])
 {
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint32_t t = (w[d] >> (2 * s)) & 0x03030303u;
-            if constexpr (BITS == 3)
-                t |= ((w[2] >> (s + 4 * d)) & 0x01010101u) << 2;
-            const uint32_t l = __builtin_amdgcn_perm(lo1, lo0, t);
-            const uint32_t h = __builtin_amdgcn_perm(hi1, hi0, t);
-            out[8 * d + 2 * s] = __builtin_amdgcn_perm(h, l, 0x05010400u);
-            out[8 * d + 2 * s + 1] = __builtin_amdgcn_perm(h, l, 0x07030602u);
-        }
+    tab[0] = __builtin_amdgcn_perm(raw[1], raw[0], 0x06040200u);
+    tab[2] = __builtin_amdgcn_perm(raw[1], raw[0], 0x07050301u);
+    tab[1] = __builtin_amdgcn_perm(raw[3], raw[2], 0x06040200u);
+    tab[3] = __builtin_amdgcn_perm(raw[3], raw[2], 0x07050301u);
 }
 
-template <int BITS>
-__device__ __forceinline__ void load_slot(const uint32_t *__restrict__ codes, long tile, int lane,
-                                          uint32_t (&w)[BITS])
+// The 8 fp16 B-operand values of MFMA step s (slot columns 8s..8s+7, natural
+// order) from one lane's slot words. FMT 2 / 3: codebook bits; 4: NVFP4.
+// Codebook: for word d = s/2 and shifts 2(s%2), 2(s%2)+1, byte b of t is the
+// code of column 16d + 4*shift + b; two v_perm lookups give its low and high
+// bytes, two more interleave them into fp16 pairs.
+// NVFP4: word s holds columns 8s..8s+7; e2m1 -> fp16 by the hardware
+// conversion (unit scale), then the e4m3 block scale in fp16 (exact: at most
+// 5 significant bits, inside the fp16 range).
+template <int FMT, int W>
+__device__ __forceinline__ half8 decode_step(const uint32_t (&w)[W], int s,
+                                             const uint32_t (&tab)[4], half2v bscale)
 {
-    const uint32_t *src = codes + (tile * 64 + lane) * BITS;
-    if constexpr (BITS == 2) {
-        const u32x2 v = *(const u32x2 *)src;
-        w[0] = v[0];
-        w[1] = v[1];
+    uint32_t o[4];
+    if constexpr (FMT == 4) {
+        const uint32_t x = w[s];
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * bscale);
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * bscale);
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * bscale);
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * bscale);
     } else {
+        const int d = s >> 1;
 #pragma unroll
-        for (int i = 0; i < BITS; ++i)
-            w[i] = src[i];
+        for (int hh = 0; hh < 2; ++hh) {
+            const int sh = 2 * (s & 1) + hh;
+            uint32_t t = (w[d] >> (2 * sh)) & 0x03030303u;
+            if constexpr (FMT == 3)
+                t |= ((w[2] >> (sh + 4 * d)) & 0x01010101u) << 2;
+            const uint32_t l = __builtin_amdgcn_perm(tab[1], tab[0], t);
+            const uint32_t h = __builtin_amdgcn_perm(tab[3], tab[2], t);
+            o[2 * hh] = __builtin_amdgcn_perm(h, l, 0x05010400u);
+            o[2 * hh + 1] = __builtin_amdgcn_perm(h, l, 0x07030602u);
+        }
+    }
+    return __builtin_bit_cast(half8, u32x4{o[0], o[1], o[2], o[3]});
+}
+
+// Wave-uniform description of the matrix part one wave computes in an item:
+// row blocks rb0, rb0+1 (16 rows each) of a matrix with G 128-column groups
+// per row, groups g0 .. g0+NG-1.
+struct WaveJob {
+    gu32p codes;
+    gu8p scales;
+    const uint16_t *lut;
+    float ts;
+    int bits;
+    int G, rb0, g0;
+};
+
+template <int CLASS>
+struct PairBuf {
+    uint32_t w[2][kWaveRB][Slot<CLASS>::W];
+    uint32_t gs[kWaveRB];     // codebook: fp16 scales of the pair's two groups
+    uint32_t bs[2][kWaveRB];  // NVFP4: the lane's two e4m3 block scales per group
+};
+
+// A wave-uniform value the compiler cannot prove uniform (it flows through
+// loop-carried state), moved to scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Buffer resource over a read-only tensor (wave-uniform base).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void GLOBAL *base)
+{
+    const uint64_t b = uniform((uint64_t)(uintptr_t)base);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)b, 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// Load pair p (groups g0+2p, g0+2p+1) of job J into b. KB: codebook bits
+// when known at compile time, 0 to read them from the job. Buffer loads with
+// the tile offset in a scalar register and one per-lane offset, so a load in
+// flight holds no address registers; one VMEM instruction per tile whatever
+// the bit width, so the waits the compiler places stay exact when the next
+// item's width differs.
+template <int CLASS, bool TWO, int KB>
+__device__ __forceinline__ void load_pair(PairBuf<CLASS> &b, const WaveJob &J, int p, int lane,
+                                          int sc_lane)
+{
+    const __amdgpu_buffer_rsrc_t rc = tensor_rsrc(J.codes);
+    const __amdgpu_buffer_rsrc_t rsc = tensor_rsrc(J.scales);
+    const int g = J.g0 + 2 * p;
+#pragma unroll
+    for (int gg = 0; gg < (TWO ? 2 : 1); ++gg)
+#pragma unroll
+        for (int i = 0; i < kWaveRB; ++i) {
+            const int tile = (J.rb0 + i) * J.G + g + gg;
+            if constexpr (CLASS == kFmtCodebook) {
+                if (KB == 3 || (KB == 0 && J.bits == 3)) {
+                    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12, tile * 768, 0);
+                    b.w[gg][i][0] = v[0];
+                    b.w[gg][i][1] = v[1];
+                    b.w[gg][i][2] = v[2];
+                } else {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane * 8, tile * 512, 0);
+                    b.w[gg][i][0] = v[0];
+                    b.w[gg][i][1] = v[1];
+                }
+            } else {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, tile * 1024, 0);
+                b.w[gg][i][0] = v[0];
+                b.w[gg][i][1] = v[1];
+                b.w[gg][i][2] = v[2];
+                b.w[gg][i][3] = v[3];
+                b.bs[gg][i] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rsc, sc_lane, (J.rb0 + i) * 16 * (J.G * 8) + (g + gg) * 8, 0);
+            }
+        }
+    if constexpr (CLASS == kFmtCodebook)
+#pragma unroll
+        for (int i = 0; i < kWaveRB; ++i) {
+            const int so = ((J.rb0 + i) * 16 * J.G + g) * 2;
+            b.gs[i] = TWO ? __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_lane, so, 0)
+                          : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, so, 0);
+        }
+}
+
+// MFMA 16x16x32: A = tokens x 32 columns from the staged activations in LDS
+// (row = token), B = 32 columns x 16 rows of W; lane (r = lane%16,
+// q = lane/16) supplies token r / W row r and columns 32q + 8s .. +7 of the
+// group at step s. Result: lane holds tokens 4(lane/16)+i of W row lane%16,
+// so each lane scales by one group scale. A rows >= R (tokens the group does
+// not have) only reach result rows that are never stored, so lanes r >= R
+// simply read row R-1.
+template <int CLASS, int FMT, bool TWO>
+__device__ __forceinline__ void process_pair(const PairBuf<CLASS> &b, int p, const _Float16 *Arow,
+                                             const uint32_t (&tab)[4], floatx4 (&acc)[kWaveRB])
+{
+#pragma unroll
+    for (int gg = 0; gg < (TWO ? 2 : 1); ++gg) {
+        const int gl = 2 * p + gg;  // group index within the item (LDS column block)
+        half8 a[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            a[s] = *(const half8 *)(Arow + gl * 128 + s * 8);
+#pragma unroll
+        for (int i = 0; i < kWaveRB; ++i) {
+            half2v bs_lo = half2v{1, 1}, bs_hi = half2v{1, 1};
+            if constexpr (FMT == 4) {
+                const _Float16 lo = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.bs[gg][i], 0);
+                const _Float16 hi = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.bs[gg][i], 1);
+                bs_lo = half2v{lo, lo};
+                bs_hi = half2v{hi, hi};
+            }
+            floatx4 cc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const half8 bv = decode_step<FMT>(b.w[gg][i], s, tab, s < 2 ? bs_lo : bs_hi);
+                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], bv, cc, 0, 0, 0);
+            }
+            if constexpr (FMT == 4) {
+                acc[i] += cc;
+            } else {
+                const uint32_t pr = b.gs[i];
+                const float f =
+                    (float)__builtin_bit_cast(_Float16, (uint16_t)(gg ? (pr >> 16) : (pr & 0xFFFFu)));
+                acc[i] += f * cc;
+            }
+            // keep the accumulation here: sunk to the end it would keep every
+            // group's MFMA result live at once
+            asm volatile("" : "+v"(acc[i]));
+        }
     }
 }
 
-// One wave: 4 row blocks (64 rows) x groups [g0, g0+ng) of one codebook
-// matrix with G groups per row. A: staged activations in LDS, row = token
-// (R rows valid), column = input column - 128 g0, row stride astride halves.
-// MFMA 16x16x32: A = tokens x 32 columns, B = 32 columns x 16 rows of W;
-// lane (r = lane%16, q = lane/16) supplies token r / W row r and columns
-// 32q + 8s' .. +7 of the group at step s'. Result lane layout: token
-// 4(lane/16) + i, W row lane%16, so one group scale per lane.
-template <int BITS, int NTB>
-__device__ __forceinline__ void gemv_codebook(const DevTensor &T, int G, int rb0, int g0, int ng,
-                                              const _Float16 *A, int astride, int R,
-                                              floatx4 (&acc)[4][NTB])
+// Pair p of the current item: the codebook bit width is a runtime property of
+// the tensor, dispatched here around the decode and MFMAs only, so the
+// buffers loaded outside stay in the same registers on both paths.
+template <int CLASS, bool TWO>
+__device__ __forceinline__ void process_any(const PairBuf<CLASS> &b, int p, int bits,
+                                            const _Float16 *Arow, const uint32_t (&tab)[4],
+                                            floatx4 (&acc)[kWaveRB])
 {
-    const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
-    const uint32_t *codes = (const uint32_t *)T.codes;
-    const uint16_t *sc = (const uint16_t *)T.scales;
-    uint32_t lo0, lo1, hi0, hi1;
-    load_lut<BITS>(T.lut, lo0, lo1, hi0, hi1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-            acc[i][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (CLASS == kFmtCodebook) {
+        if (bits == 3)
+            process_pair<CLASS, 3, TWO>(b, p, Arow, tab, acc);
+        else
+            process_pair<CLASS, 2, TWO>(b, p, Arow, tab, acc);
+    } else {
+        process_pair<CLASS, 4, TWO>(b, p, Arow, tab, acc);
+    }
+}
 
-    uint32_t wc[4][BITS], wn[4][BITS];
-    uint16_t sc_c[4], sc_n[4];
+// Pairs of 128-column groups per item.
+template <int NG>
+constexpr int kPairs = NG > 1 ? NG / 2 : 1;
+
+// All pairs of the current item, already in registers. `after(p)` runs once
+// pair p is consumed (it loads the next item's pair p+1 into the registers
+// pair p held).
+template <int CLASS, int NG, typename After>
+__device__ __forceinline__ void compute_item(const PairBuf<CLASS> (&b)[kPairs<NG>], int bits,
+                                             float ts, const _Float16 *Arow,
+                                             const uint32_t (&tab)[4], floatx4 (&acc)[kWaveRB],
+                                             After &after)
+{
+    constexpr bool TWO = NG > 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const long tile = (long)(rb0 + i) * G + g0;
-        load_slot<BITS>(codes, tile, lane, wc[i]);
-        sc_c[i] = sc[tile * 16 + r];
+    for (int i = 0; i < kWaveRB; ++i)
+        acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pp = 0; pp < kPairs<NG>; ++pp) {
+        process_any<CLASS, TWO>(b[pp], pp, bits, Arow, tab, acc);
+        after(pp);
     }
-    for (int gi = 0; gi < ng; ++gi) {
-        if (gi + 1 < ng) {
+    if constexpr (CLASS != kFmtCodebook)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const long tile = (long)(rb0 + i) * G + g0 + gi + 1;
-                load_slot<BITS>(codes, tile, lane, wn[i]);
-                sc_n[i] = sc[tile * 16 + r];
-            }
-        }
-        half8 a[NTB][4];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const int tok = tb * 16 + r;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                a[tb][s] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-                if (tok < R)
-                    a[tb][s] = *(const half8 *)(A + tok * astride + gi * 128 + q * 32 + s * 8);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t bw[16];
-            decode_slot<BITS>(wc[i], lo0, lo1, hi0, hi1, bw);
-            floatx4 c[NTB];
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-                c[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const half8 b = __builtin_bit_cast(
-                    half8, u32x4{bw[4 * s], bw[4 * s + 1], bw[4 * s + 2], bw[4 * s + 3]});
-#pragma unroll
-                for (int tb = 0; tb < NTB; ++tb)
-                    c[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tb][s], b, c[tb], 0, 0, 0);
-            }
-            const float f = (float)__builtin_bit_cast(_Float16, sc_c[i]);
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-                acc[i][tb] += f * c[tb];
-        }
-        if (gi + 1 < ng) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int b = 0; b < BITS; ++b)
-                    wc[i][b] = wn[i][b];
-                sc_c[i] = sc_n[i];
-            }
-        }
-    }
+        for (int i = 0; i < kWaveRB; ++i)
+            acc[i] *= ts;
 }
 
 // ---------------------------------------------------------------------------
 // Expert kernel: work items
 // ---------------------------------------------------------------------------
 
-// Stage R rows of fp16 activations into LDS: A[r][c] = src(r)[c], c < kc.
-__device__ __forceinline__ void stage_rows(_Float16 *A, int astride, int R, int kc,
-                                           const _Float16 *const *row_ptr)
+// One work item: gate/up (row group u = expert e's rows off..off+R-1, 128-row
+// block rb of gate and up, column split kq) or down (256-row block rb of
+// down, column split kq).
+struct Item {
+    int valid, down, e, off, R, u, rb, kq;
+};
+
+__device__ __forceinline__ Item make_item(const Params &p, const Plan *P, int ticket)
 {
-    const int chunks = kc / 8;  // 16 B each
-    for (int i = threadIdx.x; i < R * chunks; i += kThreads) {
-        const int r = i / chunks, c = (i - r * chunks) * 8;
-        *(u32x4 *)(A + r * astride + c) = *(const u32x4 *)(row_ptr[r] + c);
-    }
+    Item it{};
+    it.valid = ticket < P->n_items;
+    if (!it.valid)
+        return it;
+    const int n1 = P->n_items1;
+    it.down = ticket >= n1;
+    const int t = it.down ? ticket - n1 : ticket;
+    const int ks = it.down ? p.ks2 : p.ks1;
+    const int per_u = (it.down ? p.n_rb2 : p.n_rb1) * ks;
+    it.u = t / per_u;
+    const int rem = t - it.u * per_u;
+    it.rb = rem / ks;
+    it.kq = rem - it.rb * ks;
+    it.e = P->g_expert[it.u];
+    it.off = P->g_off[it.u];
+    it.R = P->g_rows[it.u];
+    return it;
 }
 
-template <int NTB>
-__device__ __forceinline__ void run_gemv(const DevTensor &T, int G, int rb0, int g0, int ng,
-                                         const _Float16 *A, int astride, int R,
-                                         floatx4 (&acc)[4][NTB])
+// The matrix part wave `wave` computes for item `it`: gate/up items give waves
+// 0-3 gate and 4-7 up rows (2 row blocks each), down items give each wave 2 of
+// the 16 row blocks.
+template <int NG>
+__device__ __forceinline__ WaveJob make_job(const Params &p, const Item &it, int wave)
 {
-    if (T.bits == 2)
-        gemv_codebook<2, NTB>(T, G, rb0, g0, ng, A, astride, R, acc);
-    else
-        gemv_codebook<3, NTB>(T, G, rb0, g0, ng, A, astride, R, acc);
+    const int proj = it.down ? 2 : (wave >> 2);
+    const DevTensor &T = p.tensors[it.e * 3 + proj];
+    WaveJob J;
+    J.codes = (gu32p)T.codes;
+    J.scales = (gu8p)T.scales;
+    J.lut = T.lut;
+    J.ts = T.tensor_scale;
+    J.bits = T.bits;
+    J.G = it.down ? p.I / 128 : p.H / 128;
+    J.rb0 = it.down ? it.rb * 16 + wave * kWaveRB : it.rb * 8 + (wave & 3) * kWaveRB;
+    J.g0 = it.kq * NG;
+    return J;
 }
 
-// Gate/up item: hit expert u, 128-row block rb of gate and up, column split kq.
-template <int NTB>
-__device__ void gate_up_item(const Params &p, int e, int off, int R, int u, int rb, int kq,
-                             _Float16 *A, const _Float16 **row_ptr, int *s_flag)
+struct Smem {
+    int done_tok[kGroupRows];
+    int staged[2][kExpertWaves];  // per wave: next item's rows staged (by buffer)
+    int tnext[2];                 // ticket of the next item (by buffer)
+    int flag;
+};
+
+// Last column split of a gate/up block: h = silu(g) * u over rows
+// rb*128..+127 of each token, then (codebook) h~ = (1/sqrt 128) H_128 (s_I h).
+// One wave per token; all partial-sum loads of a wave are issued together.
+__device__ void finish_h(const Params &p, int off, int R, int rb)
 {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int astride = p.kc1 + kLdsPadHalves;
-    if (tid < R)
-        row_ptr[tid] = p.xr + (size_t)(p.rows[off + tid] / p.k) * p.H + (size_t)kq * p.kc1;
-    __syncthreads();
-    stage_rows(A, astride, R, p.kc1, row_ptr);
-    __syncthreads();
-
-    const int proj = wave >> 1;                        // waves 0,1: gate; 2,3: up
-    const DevTensor T = p.tensors[e * 3 + proj];
-    const int rb0 = rb * 8 + (wave & 1) * 4;           // 16-row blocks
-    floatx4 acc[4][NTB];
-    run_gemv<NTB>(T, p.H / 128, rb0, kq * (p.kc1 / 128), p.kc1 / 128, A, astride, R, acc);
-
-    // partial sums: gu_part[kq][off + tok][proj][n]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tok = tb * 16 + 4 * (lane >> 4) + j;
-                if (tok < R) {
-                    const size_t row = (size_t)kq * p.pair_cap + off + tok;
-                    p.gu_part[(row * 2 + proj) * p.I + (rb0 + i) * 16 + (lane & 15)] = acc[i][tb][j];
-                }
-            }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        *s_flag = atomic_add_agent(&p.rb_done[u * p.n_rb1 + rb], 1u) == (uint32_t)(p.ks1 - 1);
-    __syncthreads();
-    if (!*s_flag)
-        return;
-    __threadfence();
-    // Last split of this block: h = silu(g) * u over rows rb*128..+127, then
-    // h~ = (1/sqrt 128) H_128 (s_I * h), one wave per token.
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = rb * 128 + 2 * lane;
-    for (int tok = wave; tok < R; tok += 4) {
-        float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
-        for (int s = 0; s < p.ks1; ++s) {
-            const size_t row = (size_t)s * p.pair_cap + off + tok;
-            const float *gp = p.gu_part + (row * 2 + 0) * p.I + n;
-            const float *up = p.gu_part + (row * 2 + 1) * p.I + n;
-            g0 += gp[0];
-            g1 += gp[1];
-            u0 += up[0];
-            u1 += up[1];
-        }
-        float v0 = g0 / (1.0f + expf(-g0)) * u0 * (float)p.signs_i[n];
-        float v1 = g1 / (1.0f + expf(-g1)) * u1 * (float)p.signs_i[n + 1];
-        wave_fwht128(v0, v1);
-        *(half2v *)(p.hr + (size_t)(off + tok) * p.I + n) =
-            half2v{(_Float16)(v0 * kInvSqrt128), (_Float16)(v1 * kInvSqrt128)};
+    constexpr int TPW = kGroupRows / kExpertWaves;  // tokens per wave
+    floatx2 g[TPW], u[TPW];
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+        g[ti] = floatx2{0.f, 0.f};
+        u[ti] = floatx2{0.f, 0.f};
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        atomic_add_agent(&p.h_ready[u], 1u);
-}
-
-// Down item: hit expert u, 256-row block rb of down, column split kq.
-template <int NTB>
-__device__ void down_item(const Params &p, int e, int off, int R, int u, int rb, int kq,
-                          _Float16 *A, const _Float16 **row_ptr, int *s_flag)
-{
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int astride = p.kc2 + kLdsPadHalves;
-    if (tid == 0) {
-        int ok = 1;
-        uint32_t polls = 0;
-        while (atomic_load_agent(&p.h_ready[u]) < (uint32_t)p.n_rb1) {
-            __builtin_amdgcn_s_sleep(4);
-            if (++polls > p.spin_limit) {
-                __hip_atomic_fetch_or(&p.ctr->error_word, kErrSpinLimit, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                ok = 0;
-                break;
-            }
-        }
-        *s_flag = ok;
-    }
-    if (tid < R)
-        row_ptr[tid] = p.hr + (size_t)(off + tid) * p.I + (size_t)kq * p.kc2;
-    __syncthreads();
-    if (!*s_flag)
-        return;
-    __threadfence();
-    stage_rows(A, astride, R, p.kc2, row_ptr);
-    __syncthreads();
-
-    const DevTensor T = p.tensors[e * 3 + 2];
-    const int rb0 = rb * 16 + wave * 4;
-    floatx4 acc[4][NTB];
-    run_gemv<NTB>(T, p.I / 128, rb0, kq * (p.kc2 / 128), p.kc2 / 128, A, astride, R, acc);
+    for (int s0 = 0; s0 < p.ks1; s0 += 4) {
+        uint64_t vg[TPW][4], vu[TPW][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int ti = 0; ti < TPW; ++ti)
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tok = tb * 16 + 4 * (lane >> 4) + j;
-                if (tok < R) {
-                    const size_t row = (size_t)kq * p.pair_cap + off + tok;
-                    p.y_part[row * p.H + (rb0 + i) * 16 + (lane & 15)] = acc[i][tb][j];
+            for (int s = 0; s < 4; ++s) {
+                const int tok = wave + kExpertWaves * ti;
+                vg[ti][s] = vu[ti][s] = 0;
+                if (tok < R && s0 + s < p.ks1) {
+                    const size_t row = (size_t)(s0 + s) * p.pair_cap + off + tok;
+                    vg[ti][s] = ld_coherent((const uint64_t *)(p.gu_part + (row * 2 + 0) * p.I + n));
+                    vu[ti][s] = ld_coherent((const uint64_t *)(p.gu_part + (row * 2 + 1) * p.I + n));
                 }
             }
-}
-
-__global__ __launch_bounds__(kThreads) void expert_kernel(Params p)
-{
-    extern __shared__ _Float16 A[];
-    __shared__ const _Float16 *row_ptr[kMaxTokens];
-    __shared__ int s_ticket, s_flag;
-    const Plan *P = p.plan;
-    const int n_items = P->n_items, n1 = P->n_items1;
-    int ticket = blockIdx.x;
-    uint32_t done = 0;
-    while (ticket < n_items) {
-        if (ticket < n1) {
-            const int per_u = p.n_rb1 * p.ks1;
-            const int u = ticket / per_u, rem = ticket - u * per_u;
-            const int rb = rem / p.ks1, kq = rem - rb * p.ks1;
-            const int e = P->hit_expert[u], off = P->hit_off[u], R = P->hit_rows[u];
-            if (R <= 16)
-                gate_up_item<1>(p, e, off, R, u, rb, kq, A, row_ptr, &s_flag);
-            else
-                gate_up_item<2>(p, e, off, R, u, rb, kq, A, row_ptr, &s_flag);
-        } else {
-            const int it = ticket - n1;
-            const int per_u = p.n_rb2 * p.ks2;
-            const int u = it / per_u, rem = it - u * per_u;
-            const int rb = rem / p.ks2, kq = rem - rb * p.ks2;
-            const int e = P->hit_expert[u], off = P->hit_off[u], R = P->hit_rows[u];
-            if (R <= 16)
-                down_item<1>(p, e, off, R, u, rb, kq, A, row_ptr, &s_flag);
-            else
-                down_item<2>(p, e, off, R, u, rb, kq, A, row_ptr, &s_flag);
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (s0 + s < p.ks1) {
+                    g[ti] += __builtin_bit_cast(floatx2, vg[ti][s]);
+                    u[ti] += __builtin_bit_cast(floatx2, vu[ti][s]);
+                }
+    }
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+        const int tok = wave + kExpertWaves * ti;
+        if (tok >= R)
+            break;
+        float v0 = g[ti][0] / (1.0f + expf(-g[ti][0])) * u[ti][0];
+        float v1 = g[ti][1] / (1.0f + expf(-g[ti][1])) * u[ti][1];
+        if (p.format == kFmtCodebook) {
+            v0 *= (float)p.signs_i[n];
+            v1 *= (float)p.signs_i[n + 1];
+            wave_fwht128(v0, v1);
+            v0 *= kInvSqrt128;
+            v1 *= kInvSqrt128;
         }
-        ++done;
-        __syncthreads();
-        if (threadIdx.x == 0)
-            s_ticket = (int)gridDim.x + (int)atomic_add_agent(&p.ctr->ticket, 1u);
-        __syncthreads();
-        ticket = s_ticket;
+        st_coherent((uint32_t *)(p.hr + (size_t)(off + tok) * p.I + n),
+                    __builtin_bit_cast(uint32_t, half2v{(_Float16)v0, (_Float16)v1}));
     }
-    if (threadIdx.x == 0 && done)
-        atomic_add_agent(&p.ctr->items_done, done);
 }
 
-// ---------------------------------------------------------------------------
-// Combine
-// ---------------------------------------------------------------------------
-
-__global__ __launch_bounds__(kThreads) void combine_kernel(Params p, float *__restrict__ out)
+// out[t][rb*256 + tid] = sum_j w[t][j] * sum_s y_part[s][pos(t, j)], slot order.
+__device__ void combine_rows(const Params &p, int t, int rb)
 {
-    const int t = blockIdx.y, i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= p.H)
+    if (threadIdx.x >= 256)
         return;
-    float acc = 0.0f;
-    for (int j = 0; j < p.k; ++j) {
-        const int pp = p.pos[t * p.k + j];
-        float y = 0.0f;
-        for (int s = 0; s < p.ks2; ++s)
-            y += p.y_part[((size_t)s * p.pair_cap + pp) * p.H + i];
-        acc += p.wts[t * p.k + j] * y;
+    const int row = rb * 256 + threadIdx.x;
+    float o = 0.0f;
+    for (int j0 = 0; j0 < p.k; j0 += 8) {
+        int pp[8];
+        float wj[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            pp[jj] = 0;
+            wj[jj] = 0.0f;
+            if (j0 + jj < p.k) {
+                pp[jj] = p.pos[t * p.k + j0 + jj];
+                wj[jj] = p.wts[t * p.k + j0 + jj];
+            }
+        }
+        float y[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            y[jj] = 0.0f;
+        for (int s0 = 0; s0 < p.ks2; s0 += 2) {
+            float v[8][2];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    v[jj][s] = 0.0f;
+                    if (j0 + jj < p.k && s0 + s < p.ks2)
+                        v[jj][s] = ld_coherent(
+                            &p.y_part[((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row]);
+                }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s0 + s < p.ks2)
+                        y[jj] += v[jj][s];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            if (j0 + jj < p.k)
+                o += wj[jj] * y[jj];
     }
-    out[(size_t)t * p.H + i] = acc;
+    p.out[(size_t)t * p.H + row] = o;
+}
+
+// Wait until every 128-row block of h~ of row group u is written (bounded).
+__device__ __forceinline__ bool wait_h(const Params &p, int u)
+{
+    uint32_t polls = 0;
+    while (atomic_load_agent(&p.h_ready[u]) < (uint32_t)p.n_rb1) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++polls > p.spin_limit) {
+            __hip_atomic_fetch_or(&p.ctr->error_word, kErrSpinLimit, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+    }
+    return true;
+}
+
+// Staged activations of one item, R rows x KC columns of fp16: gate/up items
+// stage the rotated activations of the group's tokens (columns kq*KC..),
+// down items stage h~ of the group's rows. Each thread holds up to ITERS
+// 16-byte chunks; indices past the end are clamped to the last chunk (a
+// duplicate write of the same value).
+template <int NG>
+struct Stage {
+    static constexpr int KC = NG * 128;
+    static constexpr int CHUNKS = KC / 8;
+    static constexpr int ITERS = (kGroupRows * CHUNKS + kExpertThreads - 1) / kExpertThreads;
+    static constexpr int ASTRIDE = KC + kLdsPadHalves;   // LDS row stride (halves)
+    static constexpr int BUF = kGroupRows * ASTRIDE;      // halves per LDS buffer
+    u32x4 v[ITERS];
+
+    __device__ __forceinline__ void issue(const Params &p, const Item &it, const int *s_tok)
+    {
+        const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
+        if (it.down) {
+            // h~ rows off..off+R-1 are consecutive: one coherent buffer
+            const _Float16 *base = p.hr + (size_t)it.off * p.I + (size_t)it.kq * KC;
+#pragma unroll
+            for (int k = 0; k < ITERS; ++k) {
+                const int i = min(tid + k * kExpertThreads, last);
+                const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+                v[k] = ld_coherent16(base, (uint32_t)((r * p.I + c) * 2));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < ITERS; ++k) {
+                const int i = min(tid + k * kExpertThreads, last);
+                const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+                const _Float16 *row = p.xr + (size_t)s_tok[it.off + r] * p.H + it.kq * KC;
+                v[k] = *(const u32x4 GLOBAL *)(row + c);
+            }
+        }
+    }
+    __device__ __forceinline__ void commit(const Item &it, _Float16 *A) const
+    {
+        const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
+#pragma unroll
+        for (int k = 0; k < ITERS; ++k) {
+            const int i = min(tid + k * kExpertThreads, last);
+            const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+            *(u32x4 *)(A + r * ASTRIDE + c) = v[k];
+        }
+    }
+};
+
+// Store an item's partial sums and publish them; the last split of a gate/up
+// block finishes h, the last down contribution of a (token, 256-row block)
+// combines it. `between` runs after the stores are acknowledged and before
+// the block barrier (it commits the next item's staged rows).
+template <typename Between>
+__device__ __forceinline__ void finish_item(const Params &p, const Item &it, const WaveJob &J,
+                                            const floatx4 (&acc)[kWaveRB], Smem &sm,
+                                            Between &between)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int proj = it.down ? 2 : ((tid >> 6) >> 2);
+#pragma unroll
+    for (int i = 0; i < kWaveRB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tok = 4 * (lane >> 4) + j;
+            if (tok < it.R) {
+                const size_t row = (size_t)it.kq * p.pair_cap + it.off + tok;
+                const int n = (J.rb0 + i) * 16 + (lane & 15);
+                float *dst = it.down ? &p.y_part[row * p.H + n]
+                                     : &p.gu_part[(row * 2 + proj) * p.I + n];
+                st_coherent(dst, acc[i][j]);
+            }
+        }
+    wait_stores();
+    between();
+    __syncthreads();
+    if (!it.down) {
+        if (tid == 0)
+            sm.flag = atomic_add_agent(&p.rb_done[it.u * p.n_rb1 + it.rb], 1u) ==
+                      (uint32_t)(p.ks1 - 1);
+        __syncthreads();
+        if (sm.flag) {
+            finish_h(p, it.off, it.R, it.rb);
+            wait_stores();
+            __syncthreads();
+            if (tid == 0)
+                atomic_add_agent(&p.h_ready[it.u], 1u);
+        }
+        return;
+    }
+    if (tid < it.R) {
+        const int t = p.rows[it.off + tid] / p.k;
+        const uint32_t old = atomic_add_agent(&p.comb[t * p.n_rb2 + it.rb], 1u);
+        sm.done_tok[tid] = old == (uint32_t)(p.k * p.ks2 - 1) ? t : -1;
+    }
+    __syncthreads();
+    for (int tok = 0; tok < it.R; ++tok)
+        if (sm.done_tok[tok] >= 0)
+            combine_rows(p, sm.done_tok[tok], it.rb);
+}
+
+// The codebook of job J as stored, read through a buffer resource whose size
+// is the codebook's: for a 2-bit codebook the upper 8 bytes are out of range
+// and read as zero without touching memory.
+__device__ __forceinline__ u32x4 load_lut_raw(const WaveJob &J)
+{
+    const uint64_t base = uniform((uint64_t)(uintptr_t)J.lut);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(uintptr_t)base, 0, 2 << J.bits, 0x00020000);
+    const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0);
+    const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(r, 8, 0, 0);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Persistent block: pulls tickets and pipelines items. Item i computes from
+// registers filled during item i-1: while it runs, the next item's codebook,
+// activation rows (into the other LDS staging buffer) and weight pairs are
+// loaded, pair p+1 as soon as pair p of item i is consumed, so every load has
+// at least one pair's compute time before the item's tail waits for it. The
+// ticket of item i+2 is claimed during item i and published at its tail.
+// Staging buffer, ticket slot and staged flags alternate between items, so
+// every value a wave reads after a barrier is written again only after the
+// next barrier.
+template <int CLASS, int NG>
+__global__ __launch_bounds__(kExpertThreads) void expert_kernel(Params p)
+{
+    extern __shared__ _Float16 Abuf[];  // two staging buffers of min(m, 16) rows
+    __shared__ Smem sm;
+    __shared__ int s_tok[kMaxPairs];    // token of each bucket row
+    constexpr bool TWO = NG > 1;
+    constexpr int NP = kPairs<NG>;
+    using St = Stage<NG>;
+    const Plan *P = p.plan;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int buf_halves = min(P->m, kGroupRows) * St::ASTRIDE;
+
+    for (int i = tid; i < P->m * p.k; i += kExpertThreads)
+        s_tok[i] = p.rows[i] / p.k;
+    if (tid == 0)
+        sm.tnext[0] = (int)gridDim.x + (int)atomic_add_agent(&p.ctr->ticket, 1u);
+    __syncthreads();
+
+    Item cur = make_item(p, P, blockIdx.x);
+    uint32_t done = 0;
+    if (cur.valid) {
+        int buf = 0;
+        PairBuf<CLASS> b[NP];
+        St st;
+        WaveJob J = make_job<NG>(p, cur, wave);
+        int sc_lane = CLASS == kFmtCodebook ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+        u32x4 lut = u32x4{0, 0, 0, 0};
+        // first item: nothing was prefetched
+        bool ok = true;
+        if (cur.down) {
+            if (tid == 0)
+                sm.flag = wait_h(p, cur.u);
+            __syncthreads();
+            ok = sm.flag != 0;
+        }
+        st.issue(p, cur, s_tok);
+        if constexpr (CLASS == kFmtCodebook)
+            lut = load_lut_raw(J);
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+            load_pair<CLASS, TWO, 0>(b[pp], J, pp, lane, sc_lane);
+        st.commit(cur, Abuf);
+        __syncthreads();
+
+        while (true) {
+            uint32_t t_after = 0;
+            if (tid == 0)
+                t_after = gridDim.x + atomic_add_agent(&p.ctr->ticket, 1u);
+            const Item nxt = make_item(p, P, uniform(sm.tnext[buf]));
+            WaveJob JN{};
+            if (nxt.valid)
+                JN = make_job<NG>(p, nxt, wave);
+            const int sc_next = CLASS == kFmtCodebook ? r16 * JN.G * 2 : r16 * JN.G * 8 + 2 * q;
+            uint32_t tab[4] = {0, 0, 0, 0};
+            if constexpr (CLASS == kFmtCodebook)
+                lut_tables(lut, tab);
+
+            // next item, first part: its rows of activations (a down item's
+            // rows only once its h is complete), its codebook, its first pair
+            bool staged = false;
+            PairBuf<CLASS> nb[NP];
+            if (nxt.valid) {
+                staged = !nxt.down ||
+                         (uint32_t)uniform((int)atomic_load_agent(&p.h_ready[nxt.u])) >=
+                             (uint32_t)p.n_rb1;
+                if (staged)
+                    st.issue(p, nxt, s_tok);
+                if constexpr (CLASS == kFmtCodebook)
+                    lut = load_lut_raw(JN);
+                load_pair<CLASS, TWO, 0>(nb[0], JN, 0, lane, sc_next);
+            }
+            auto after = [&](int pp) {
+                if (nxt.valid && pp + 1 < NP)
+                    load_pair<CLASS, TWO, 0>(nb[pp + 1], JN, pp + 1, lane, sc_next);
+            };
+            const _Float16 *Arow = Abuf + buf * buf_halves + min(r16, cur.R - 1) * St::ASTRIDE + q * 32;
+            floatx4 acc[kWaveRB];
+            compute_item<CLASS, NG>(b, J.bits, J.ts, Arow, tab, acc, after);
+
+            auto between = [&]() {
+                if (staged)
+                    st.commit(nxt, Abuf + (buf ^ 1) * buf_halves);
+                if (lane == 0)
+                    sm.staged[buf ^ 1][wave] = staged;
+                if (tid == 0)
+                    sm.tnext[buf ^ 1] = (int)t_after;
+            };
+            if (ok) {
+                finish_item(p, cur, J, acc, sm, between);
+            } else {
+                between();
+            }
+            ++done;
+            __syncthreads();
+            if (!nxt.valid)
+                break;
+            buf ^= 1;
+            bool all_staged = true;
+#pragma unroll
+            for (int w = 0; w < kExpertWaves; ++w)
+                all_staged = all_staged && sm.staged[buf][w] != 0;
+            cur = nxt;
+            J = JN;
+            sc_lane = sc_next;
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp)
+                b[pp] = nb[pp];
+            ok = true;
+            if (!all_staged) {
+                // some wave could not stage its share of the rows (h not yet
+                // complete when it looked): wait and stage them all now
+                if (cur.down) {
+                    if (tid == 0)
+                        sm.flag = wait_h(p, cur.u);
+                    __syncthreads();
+                    ok = sm.flag != 0;
+                }
+                st.issue(p, cur, s_tok);
+                st.commit(cur, Abuf + buf * buf_halves);
+                __syncthreads();
+            }
+        }
+    }
+    if (tid == 0 && done)
+        atomic_add_agent(&p.ctr->items_done, done);
 }
 
 // ---------------------------------------------------------------------------
@@ -588,26 +987,49 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Params p, float *__re
 hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits, int m,
                         hipStream_t s)
 {
-    route_kernel<<<dim3(m), dim3(kThreads), 0, s>>>(p, x, logits, m);
+    const int tasks = m * (p.H / 128);
+    route_kernel<<<dim3(1 + (tasks + kRouteWaves - 1) / kRouteWaves), dim3(kRouteThreads), 0, s>>>(
+        p, x, logits, m);
     return hipGetLastError();
+}
+
+template <int CLASS, int NG>
+static void *expert_fn()
+{
+    return (void *)expert_kernel<CLASS, NG>;
+}
+
+// The expert kernel specialised for the format class and the groups per
+// column split (1, 2, 4 or 8).
+static void *expert_kernel_for(int format, int ng)
+{
+    if (format == kFmtCodebook) {
+        switch (ng) {
+        case 8: return expert_fn<kFmtCodebook, 8>();
+        case 4: return expert_fn<kFmtCodebook, 4>();
+        case 2: return expert_fn<kFmtCodebook, 2>();
+        default: return expert_fn<kFmtCodebook, 1>();
+        }
+    }
+    switch (ng) {
+    case 8: return expert_fn<kFmtNvfp4, 8>();
+    case 4: return expert_fn<kFmtNvfp4, 4>();
+    case 2: return expert_fn<kFmtNvfp4, 2>();
+    default: return expert_fn<kFmtNvfp4, 1>();
+    }
 }
 
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s)
 {
-    expert_kernel<<<dim3(grid), dim3(kThreads), lds_bytes, s>>>(p);
-    return hipGetLastError();
+    void *fn = expert_kernel_for(p.format, p.kc1 / 128);
+    void *args[] = {const_cast<Params *>(&p)};
+    return hipLaunchKernel(fn, dim3(grid), dim3(kExpertThreads), args, lds_bytes, s);
 }
 
-hipError_t launch_combine(const Params &p, float *out, int m, hipStream_t s)
+hipError_t expert_occupancy(int format, int ng, int *blocks_per_cu, size_t lds_bytes)
 {
-    combine_kernel<<<dim3((p.H + kThreads - 1) / kThreads, m), dim3(kThreads), 0, s>>>(p, out);
-    return hipGetLastError();
-}
-
-hipError_t expert_occupancy(int *blocks_per_cu, size_t lds_bytes)
-{
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, expert_kernel, kThreads,
-                                                        lds_bytes);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, expert_kernel_for(format, ng),
+                                                        kExpertThreads, lds_bytes);
 }
 
 }  // namespace moe

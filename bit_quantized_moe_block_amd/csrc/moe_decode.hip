@@ -62,12 +62,14 @@ static moe_status fail(moe_status s, const char *fmt, ...)
 
 static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Columns per split: 128 x the largest divisor d of C/128 with d <= 8.
-static int split_cols(int C)
+// Columns per split, shared by the gate/up (hidden) and down (inter) GEMVs:
+// 128 x the largest power of two d <= 8 dividing both H/128 and I/128 (the
+// expert kernel is specialised for 1, 2, 4 or 8 groups per split).
+static int split_cols(int H, int I)
 {
-    int g = C / 128, best = 1;
-    for (int d = 1; d <= 8; ++d)
-        if (g % d == 0)
+    int best = 1;
+    for (int d = 1; d <= 8; d *= 2)
+        if ((H / 128) % d == 0 && (I / 128) % d == 0)
             best = d;
     return 128 * best;
 }
@@ -118,7 +120,7 @@ static moe_status validate(const moe_decode_config *c)
                                 t.bits);
                 if (!t.lut)
                     return fail(MOE_E_INVALID, "expert %d projection %d: NULL lut", e, p);
-                if (!aligned(t.codes, 16) || !aligned(t.scales, 2) || !aligned(t.lut, 4))
+                if (!aligned(t.codes, 16) || !aligned(t.scales, 16) || !aligned(t.lut, 4))
                     return fail(MOE_E_INVALID, "expert %d projection %d: misaligned pointer", e, p);
             } else {
                 if (t.bits != 4)
@@ -130,8 +132,6 @@ static moe_status validate(const moe_decode_config *c)
             }
         }
     }
-    if (!cb)
-        return fail(MOE_E_UNSUPPORTED, "NVFP4 experts are not supported by this build yet");
     return MOE_OK;
 }
 
@@ -154,9 +154,8 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.H = cfg->hidden;
     p.I = cfg->inter;
     p.max_tokens = cfg->max_tokens;
-    p.kc1 = split_cols(p.H);
+    p.kc1 = p.kc2 = split_cols(p.H, p.I);
     p.ks1 = p.H / p.kc1;
-    p.kc2 = split_cols(p.I);
     p.ks2 = p.I / p.kc2;
     p.n_rb1 = p.I / 128;
     p.n_rb2 = p.H / 256;
@@ -193,8 +192,8 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     const size_t o_ids = take(4 * PC), o_wts = take(4 * PC), o_counts = take(4 * E),
                  o_offsets = take(4 * (E + 1)), o_rows = take(4 * PC), o_pos = take(4 * PC);
     const size_t o_plan = take(sizeof(Plan));
-    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(4 * E * p.n_rb1),
-                 o_hready = take(4 * E);
+    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(4 * kMaxGroups * p.n_rb1),
+                 o_hready = take(4 * kMaxGroups), o_comb = take(4 * M * p.n_rb2);
     const size_t ctr_end = off;
     const size_t o_xr = take(2 * M * H), o_gu = take(4 * (size_t)p.ks1 * PC * 2 * I),
                  o_hr = take(2 * PC * I), o_y = take(4 * (size_t)p.ks2 * PC * H);
@@ -215,6 +214,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.ctr = (Counters *)(base + o_ctr);
     p.rb_done = (uint32_t *)(base + o_rbdone);
     p.h_ready = (uint32_t *)(base + o_hready);
+    p.comb = (uint32_t *)(base + o_comb);
     p.xr = (_Float16 *)(base + o_xr);
     p.gu_part = (float *)(base + o_gu);
     p.hr = (_Float16 *)(base + o_hr);
@@ -239,9 +239,10 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     h->bpc.assign(M + 1, 0);
     h->lds.assign(M + 1, 0);
     for (int m = 1; m <= (int)M; ++m) {
-        const size_t lds = (size_t)m * (kc + kLdsPadHalves) * sizeof(_Float16);
+        // two staging buffers (the next item's rows load while this one computes)
+        const size_t lds = 2 * (size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) * sizeof(_Float16);
         int bpc = 0;
-        err = expert_occupancy(&bpc, lds);
+        err = expert_occupancy(p.format, p.kc1 / 128, &bpc, lds);
         if (err != hipSuccess || bpc < 1)
             return cleanup(fail(MOE_E_UNSUPPORTED, "expert kernel cannot be resident with %zu B LDS",
                                 lds));
@@ -274,13 +275,14 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
         return fail(MOE_E_STREAM, "handle is bound to another stream");
     h->bound = true;
     h->stream = s;
-    HIP_TRY(launch_route(h->p, (const uint16_t *)x_bf16, logits, m, s));
+    Params p = h->p;
+    p.out = out;
+    HIP_TRY(launch_route(p, (const uint16_t *)x_bf16, logits, m, s));
     if (h->ev_begin)
         HIP_TRY(hipEventRecord(h->ev_begin, s));
-    HIP_TRY(launch_expert(h->p, h->grid[m], h->lds[m], s));
+    HIP_TRY(launch_expert(p, h->grid[m], h->lds[m], s));
     if (h->ev_end)
         HIP_TRY(hipEventRecord(h->ev_end, s));
-    HIP_TRY(launch_combine(h->p, out, m, s));
     h->ran = true;
     h->last_m = m;
     return MOE_OK;

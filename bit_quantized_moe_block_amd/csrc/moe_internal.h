@@ -9,8 +9,11 @@ namespace moe {
 constexpr int kThreads = 256;       // every kernel: 4 wave64s
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
-constexpr int kMaxTokens = 32;      // at most two 16-row MFMA token blocks
+constexpr int kMaxTokens = 32;
 constexpr int kMaxPairs = kMaxTokens * kMaxTopK;
+constexpr int kGroupRows = 16;      // rows of one MFMA token block
+// Row groups: each hit expert's bucket split into groups of <= 16 rows.
+constexpr int kMaxGroups = kMaxExperts + kMaxPairs / kGroupRows;
 constexpr int kLdsPadHalves = 8;    // 16 B row padding of the staged activations
 
 constexpr int kFmtCodebook = 1;
@@ -28,23 +31,24 @@ struct DevTensor {
     int32_t bits;
 };
 
-// Routing result of one run, written by the route kernel (its last block).
+// Routing result of one run, written by block 0 of the route kernel.
 struct Plan {
     int32_t m;
     int32_t n_hit;         // experts with >= 1 row
+    int32_t n_groups;      // row groups (<= 16 rows each)
     int32_t n_items1;      // gate/up work items
     int32_t n_items;       // all work items
-    int32_t hit_expert[kMaxExperts];  // expert id of hit expert u (ascending)
-    int32_t hit_off[kMaxExperts];     // first row of u in the bucket row list
-    int32_t hit_rows[kMaxExperts];    // R_u
+    int32_t pad[3];
+    int32_t g_expert[kMaxGroups];  // expert of group u (groups in expert order)
+    int32_t g_off[kMaxGroups];     // first row of u in the bucket row list
+    int32_t g_rows[kMaxGroups];    // rows of u (1..16)
 };
 
 struct Counters {
-    uint32_t route_done;   // route blocks finished (reset by the last one)
     uint32_t ticket;       // dynamic work-item tickets handed out
     uint32_t items_done;   // work items completed (statistics)
     uint32_t error_word;   // kErr* bits
-    uint32_t pad[4];
+    uint32_t pad[5];
 };
 
 // Everything a kernel needs, passed by value.
@@ -56,6 +60,7 @@ struct Params {
     int32_t n_rb2;         // H / 256 down row blocks of 256
     int32_t pair_cap;      // max_tokens * k
     uint32_t spin_limit;   // polls before a dependency wait gives up
+    float *out;            // [m][H] result of the current launch
     const DevTensor *tensors;   // [E*3]
     const int8_t *signs_h;      // [H]
     const int8_t *signs_i;      // [I]
@@ -71,16 +76,16 @@ struct Params {
     _Float16 *hr;          // [pair_cap][I] rotated SiLU(g)*u (fp16)
     float *y_part;         // [ks2][pair_cap][H] down partial sums
     Counters *ctr;
-    uint32_t *rb_done;     // [E][n_rb1] finished column splits per row block
-    uint32_t *h_ready;     // [E] finished row blocks of h per hit expert
+    uint32_t *rb_done;     // [kMaxGroups][n_rb1] finished column splits per row block
+    uint32_t *h_ready;     // [kMaxGroups] finished row blocks of h per row group
+    uint32_t *comb;        // [max_tokens][n_rb2] finished down contributions per token block
 };
 
 // Kernel launchers (kernels.hip).
 hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits, int m,
                         hipStream_t s);
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s);
-hipError_t launch_combine(const Params &p, float *out, int m, hipStream_t s);
 // Occupancy of the expert kernel for a given dynamic LDS size.
-hipError_t expert_occupancy(int *blocks_per_cu, size_t lds_bytes);
+hipError_t expert_occupancy(int format, int ng, int *blocks_per_cu, size_t lds_bytes);
 
 }  // namespace moe

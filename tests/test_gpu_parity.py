@@ -215,3 +215,25 @@ def test_tokens_fewer_than_max_tokens():
             assert rel_err(out, ref["out"]) <= REL_TOL
     finally:
         layer.close()
+
+
+NVFP4_GRID = [
+    (small_workload("fp4a", 8, 2, 256, 128, fmt="nvfp4", bits_mix="nvfp4", config_id=401), 1),
+    (small_workload("fp4b", 16, 4, 1024, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=402), 9),
+    (small_workload("fp4c", 32, 3, 512, 384, fmt="nvfp4", bits_mix="nvfp4", config_id=403), 24),
+]
+
+
+@pytest.mark.parametrize("w,m", NVFP4_GRID, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_nvfp4_small(w, m):
+    parity(gen.make_case(w, m))
+
+
+@pytest.mark.parametrize("m", [2, 8])
+def test_nvfp4_full_sampled(m):
+    w = WORKLOADS["nvfp4"]
+    rid, _ = oracle.route(gen.make_logits(w, 0, m), w.top_k)
+    d = gen.make_layer(w, 0)
+    d["workload"] = w
+    case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
+    parity(case, tokens=sorted(set([0, m - 1])), max_tokens=8)
