@@ -8,8 +8,8 @@
 //                starts clean without a memset). Blocks 1..: one wave per
 //                (token, 128-column block) rotates x (codebook) or converts
 //                it to fp16 (NVFP4). No block waits on another.
-// expert_kernel  persistent grid pulling work-item tickets, no grid-wide
-//                barrier. Gate/up items (one row group, 128 rows of gate and
+// expert_kernel  persistent grid, work items assigned round robin (no shared
+//                ticket counter), no grid-wide barrier. Gate/up items (one row group, 128 rows of gate and
 //                of up, one column split) write partial sums; the last split
 //                of a 128-row block finishes SiLU(g)*u and the 128-point
 //                rotation of h. Down items (256 rows of down, one column
@@ -262,16 +262,16 @@ __device__ void route_block(const Params &p, const float *__restrict__ logits, i
         P->n_groups = ngroups;
         P->n_items1 = n1;
         P->n_items = n1 + ngroups * p.n_rb2 * p.ks2;
-        p.ctr->ticket = 0;
-        p.ctr->items_done = 0;
+        for (int i = 0; i < kDoneSlots; ++i)
+            p.ctr->items_done[i] = 0;
         p.ctr->error_word = 0;
     }
     for (int i = tid; i < ngroups * p.n_rb1; i += kRouteThreads)
-        p.rb_done[i] = 0;
+        p.rb_done[i * kCtrStride] = 0;
     for (int i = tid; i < ngroups; i += kRouteThreads)
-        p.h_ready[i] = 0;
+        p.h_ready[i * kCtrStride] = 0;
     for (int i = tid; i < m * p.n_rb2; i += kRouteThreads)
-        p.comb[i] = 0;
+        p.comb[i * kCtrStride] = 0;
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
@@ -313,8 +313,8 @@ typedef const uint8_t GLOBAL *gu8p;
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Row blocks (16 rows each) one wave computes; waves per expert-kernel block.
-constexpr int kWaveRB = 2;
-constexpr int kExpertThreads = 512;
+constexpr int kWaveRB = 4;
+constexpr int kExpertThreads = 256;
 constexpr int kExpertWaves = kExpertThreads / 64;
 
 // Slot words held per tile: codebook up to 3 (2-bit tensors use 2), NVFP4 4.
@@ -383,11 +383,13 @@ struct WaveJob {
     int G, rb0, g0;
 };
 
+// One register buffer of weight data: one 128-column group of the wave's
+// kWaveRB row blocks (tiles), with the lane's scales of each tile: the fp16
+// group scale (codebook) or the two e4m3 block scales (NVFP4).
 template <int CLASS>
-struct PairBuf {
-    uint32_t w[2][kWaveRB][Slot<CLASS>::W];
-    uint32_t gs[kWaveRB];     // codebook: fp16 scales of the pair's two groups
-    uint32_t bs[2][kWaveRB];  // NVFP4: the lane's two e4m3 block scales per group
+struct GroupBuf {
+    uint32_t w[kWaveRB][Slot<CLASS>::W];
+    uint32_t sc[kWaveRB];
 };
 
 // A wave-uniform value the compiler cannot prove uniform (it flows through
@@ -407,52 +409,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void GLOBAL 
     return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)b, 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Load pair p (groups g0+2p, g0+2p+1) of job J into b. KB: codebook bits
+// Load group j (absolute group g0 + j) of job J into b. KB: codebook bits
 // when known at compile time, 0 to read them from the job. Buffer loads with
 // the tile offset in a scalar register and one per-lane offset, so a load in
 // flight holds no address registers; one VMEM instruction per tile whatever
 // the bit width, so the waits the compiler places stay exact when the next
 // item's width differs.
-template <int CLASS, bool TWO, int KB>
-__device__ __forceinline__ void load_pair(PairBuf<CLASS> &b, const WaveJob &J, int p, int lane,
-                                          int sc_lane)
+template <int CLASS, int KB>
+__device__ __forceinline__ void load_group(GroupBuf<CLASS> &b, const WaveJob &J, int j, int lane,
+                                           int sc_lane)
 {
     const __amdgpu_buffer_rsrc_t rc = tensor_rsrc(J.codes);
     const __amdgpu_buffer_rsrc_t rsc = tensor_rsrc(J.scales);
-    const int g = J.g0 + 2 * p;
+    const int g = J.g0 + j;
 #pragma unroll
-    for (int gg = 0; gg < (TWO ? 2 : 1); ++gg)
-#pragma unroll
-        for (int i = 0; i < kWaveRB; ++i) {
-            const int tile = (J.rb0 + i) * J.G + g + gg;
-            if constexpr (CLASS == kFmtCodebook) {
-                if (KB == 3 || (KB == 0 && J.bits == 3)) {
-                    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12, tile * 768, 0);
-                    b.w[gg][i][0] = v[0];
-                    b.w[gg][i][1] = v[1];
-                    b.w[gg][i][2] = v[2];
-                } else {
-                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane * 8, tile * 512, 0);
-                    b.w[gg][i][0] = v[0];
-                    b.w[gg][i][1] = v[1];
-                }
+    for (int i = 0; i < kWaveRB; ++i) {
+        const int tile = (J.rb0 + i) * J.G + g;
+        if constexpr (CLASS == kFmtCodebook) {
+            if (KB == 3 || (KB == 0 && J.bits == 3)) {
+                const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12, tile * 768, 0);
+                b.w[i][0] = v[0];
+                b.w[i][1] = v[1];
+                b.w[i][2] = v[2];
             } else {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, tile * 1024, 0);
-                b.w[gg][i][0] = v[0];
-                b.w[gg][i][1] = v[1];
-                b.w[gg][i][2] = v[2];
-                b.w[gg][i][3] = v[3];
-                b.bs[gg][i] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rsc, sc_lane, (J.rb0 + i) * 16 * (J.G * 8) + (g + gg) * 8, 0);
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane * 8, tile * 512, 0);
+                b.w[i][0] = v[0];
+                b.w[i][1] = v[1];
             }
+            // scales[row][g], row = 16 (rb0 + i) + lane % 16
+            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane,
+                                                           ((J.rb0 + i) * 16 * J.G + g) * 2, 0);
+        } else {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, tile * 1024, 0);
+            b.w[i][0] = v[0];
+            b.w[i][1] = v[1];
+            b.w[i][2] = v[2];
+            b.w[i][3] = v[3];
+            // scales[row][8 g + 2 (lane / 16) + {0, 1}]
+            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane,
+                                                           (J.rb0 + i) * 16 * (J.G * 8) + g * 8, 0);
         }
-    if constexpr (CLASS == kFmtCodebook)
-#pragma unroll
-        for (int i = 0; i < kWaveRB; ++i) {
-            const int so = ((J.rb0 + i) * 16 * J.G + g) * 2;
-            b.gs[i] = TWO ? __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_lane, so, 0)
-                          : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, so, 0);
-        }
+    }
 }
 
 // MFMA 16x16x32: A = tokens x 32 columns from the staged activations in LDS
@@ -461,87 +458,78 @@ __device__ __forceinline__ void load_pair(PairBuf<CLASS> &b, const WaveJob &J, i
 // group at step s. Result: lane holds tokens 4(lane/16)+i of W row lane%16,
 // so each lane scales by one group scale. A rows >= R (tokens the group does
 // not have) only reach result rows that are never stored, so lanes r >= R
-// simply read row R-1.
-template <int CLASS, int FMT, bool TWO>
-__device__ __forceinline__ void process_pair(const PairBuf<CLASS> &b, int p, const _Float16 *Arow,
-                                             const uint32_t (&tab)[4], floatx4 (&acc)[kWaveRB])
+// simply read row R-1. j = group index within the item (LDS column block).
+template <int CLASS, int FMT>
+__device__ __forceinline__ void process_group(const GroupBuf<CLASS> &b, int j, const _Float16 *Arow,
+                                              const uint32_t (&tab)[4], floatx4 (&acc)[kWaveRB])
 {
+    half8 a[4];
 #pragma unroll
-    for (int gg = 0; gg < (TWO ? 2 : 1); ++gg) {
-        const int gl = 2 * p + gg;  // group index within the item (LDS column block)
-        half8 a[4];
+    for (int s = 0; s < 4; ++s)
+        a[s] = *(const half8 *)(Arow + j * 128 + s * 8);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            a[s] = *(const half8 *)(Arow + gl * 128 + s * 8);
-#pragma unroll
-        for (int i = 0; i < kWaveRB; ++i) {
-            half2v bs_lo = half2v{1, 1}, bs_hi = half2v{1, 1};
-            if constexpr (FMT == 4) {
-                const _Float16 lo = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.bs[gg][i], 0);
-                const _Float16 hi = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.bs[gg][i], 1);
-                bs_lo = half2v{lo, lo};
-                bs_hi = half2v{hi, hi};
-            }
-            floatx4 cc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const half8 bv = decode_step<FMT>(b.w[gg][i], s, tab, s < 2 ? bs_lo : bs_hi);
-                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], bv, cc, 0, 0, 0);
-            }
-            if constexpr (FMT == 4) {
-                acc[i] += cc;
-            } else {
-                const uint32_t pr = b.gs[i];
-                const float f =
-                    (float)__builtin_bit_cast(_Float16, (uint16_t)(gg ? (pr >> 16) : (pr & 0xFFFFu)));
-                acc[i] += f * cc;
-            }
-            // keep the accumulation here: sunk to the end it would keep every
-            // group's MFMA result live at once
-            asm volatile("" : "+v"(acc[i]));
+    for (int i = 0; i < kWaveRB; ++i) {
+        half2v bs_lo = half2v{1, 1}, bs_hi = half2v{1, 1};
+        if constexpr (FMT == 4) {
+            const _Float16 lo = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.sc[i], 0);
+            const _Float16 hi = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.sc[i], 1);
+            bs_lo = half2v{lo, lo};
+            bs_hi = half2v{hi, hi};
         }
+        floatx4 cc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const half8 bv = decode_step<FMT>(b.w[i], s, tab, s < 2 ? bs_lo : bs_hi);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], bv, cc, 0, 0, 0);
+        }
+        if constexpr (FMT == 4) {
+            acc[i] += cc;
+        } else {
+            const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[i]);
+            acc[i] += f * cc;
+        }
+        // keep the accumulation here: sunk to the end it would keep every
+        // group's MFMA result live at once
+        asm volatile("" : "+v"(acc[i]));
     }
 }
 
-// Pair p of the current item: the codebook bit width is a runtime property of
-// the tensor, dispatched here around the decode and MFMAs only, so the
+// Group j of the current item: the codebook bit width is a runtime property
+// of the tensor, dispatched here around the decode and MFMAs only, so the
 // buffers loaded outside stay in the same registers on both paths.
-template <int CLASS, bool TWO>
-__device__ __forceinline__ void process_any(const PairBuf<CLASS> &b, int p, int bits,
+template <int CLASS>
+__device__ __forceinline__ void process_any(const GroupBuf<CLASS> &b, int j, int bits,
                                             const _Float16 *Arow, const uint32_t (&tab)[4],
                                             floatx4 (&acc)[kWaveRB])
 {
     if constexpr (CLASS == kFmtCodebook) {
         if (bits == 3)
-            process_pair<CLASS, 3, TWO>(b, p, Arow, tab, acc);
+            process_group<CLASS, 3>(b, j, Arow, tab, acc);
         else
-            process_pair<CLASS, 2, TWO>(b, p, Arow, tab, acc);
+            process_group<CLASS, 2>(b, j, Arow, tab, acc);
     } else {
-        process_pair<CLASS, 4, TWO>(b, p, Arow, tab, acc);
+        process_group<CLASS, 4>(b, j, Arow, tab, acc);
     }
 }
 
-// Pairs of 128-column groups per item.
-template <int NG>
-constexpr int kPairs = NG > 1 ? NG / 2 : 1;
-
-// All pairs of the current item, already in registers. `after(p)` runs once
-// pair p is consumed (it loads the next item's pair p+1 into the registers
-// pair p held).
+// All NG groups of the current item from two register buffers used in turn.
+// `after(j, buf)` runs once group j is consumed, with the buffer that held
+// it: it loads what that buffer holds next (group j+2 of this item, or one
+// of the next item's first two groups).
 template <int CLASS, int NG, typename After>
-__device__ __forceinline__ void compute_item(const PairBuf<CLASS> (&b)[kPairs<NG>], int bits,
+__device__ __forceinline__ void compute_item(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
                                              float ts, const _Float16 *Arow,
                                              const uint32_t (&tab)[4], floatx4 (&acc)[kWaveRB],
                                              After &after)
 {
-    constexpr bool TWO = NG > 1;
 #pragma unroll
     for (int i = 0; i < kWaveRB; ++i)
         acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int pp = 0; pp < kPairs<NG>; ++pp) {
-        process_any<CLASS, TWO>(b[pp], pp, bits, Arow, tab, acc);
-        after(pp);
+    for (int j = 0; j < NG; ++j) {
+        GroupBuf<CLASS> &b = (j & 1) ? bB : bA;
+        process_any<CLASS>(b, j, bits, Arow, tab, acc);
+        after(j, b);
     }
     if constexpr (CLASS != kFmtCodebook)
 #pragma unroll
@@ -560,107 +548,140 @@ struct Item {
     int valid, down, e, off, R, u, rb, kq;
 };
 
-__device__ __forceinline__ Item make_item(const Params &p, const Plan *P, int ticket)
+// Row-group table of the plan, cached in LDS by every block: expert, first
+// bucket row and rows of group u.
+struct GroupLds {
+    int expert[kMaxGroups], off[kMaxGroups], rows[kMaxGroups];
+};
+
+__device__ __forceinline__ Item make_item(const Params &p, int n_items, int n_items1,
+                                          const GroupLds &gl, int ticket)
 {
     Item it{};
-    it.valid = ticket < P->n_items;
+    it.valid = ticket < n_items;
     if (!it.valid)
         return it;
-    const int n1 = P->n_items1;
-    it.down = ticket >= n1;
-    const int t = it.down ? ticket - n1 : ticket;
+    it.down = ticket >= n_items1;
+    const int t = it.down ? ticket - n_items1 : ticket;
     const int ks = it.down ? p.ks2 : p.ks1;
     const int per_u = (it.down ? p.n_rb2 : p.n_rb1) * ks;
     it.u = t / per_u;
     const int rem = t - it.u * per_u;
     it.rb = rem / ks;
     it.kq = rem - it.rb * ks;
-    it.e = P->g_expert[it.u];
-    it.off = P->g_off[it.u];
-    it.R = P->g_rows[it.u];
+    it.e = uniform(gl.expert[it.u]);
+    it.off = uniform(gl.off[it.u]);
+    it.R = uniform(gl.rows[it.u]);
     return it;
 }
 
-// The matrix part wave `wave` computes for item `it`: gate/up items give waves
-// 0-3 gate and 4-7 up rows (2 row blocks each), down items give each wave 2 of
-// the 16 row blocks.
-template <int NG>
-__device__ __forceinline__ WaveJob make_job(const Params &p, const Item &it, int wave)
+// The stored-tensor descriptor of the matrix wave `wave` computes for item
+// `it`, fetched with vector loads (they are waited on through vmcnt, in
+// order with the weight prefetches, instead of sharing lgkmcnt with the LDS
+// reads of the inner loop). An invalid item reads descriptor 0.
+struct DescRaw {
+    u32x4 d0, d1;
+};
+
+__device__ __forceinline__ int item_proj(const Item &it, int wave)
 {
-    const int proj = it.down ? 2 : (wave >> 2);
-    const DevTensor &T = p.tensors[it.e * 3 + proj];
+    // gate/up items: the first half of the waves gate, the second half up
+    return it.down ? 2 : wave / (kExpertWaves / 2);
+}
+
+__device__ __forceinline__ DescRaw load_desc(const Params &p, const Item &it, int wave)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<DevTensor *>(p.tensors), 0, 0x7FFFFFFF, 0x00020000);
+    const int idx = it.valid ? it.e * 3 + item_proj(it, wave) : 0;
+    DescRaw d;
+    d.d0 = __builtin_amdgcn_raw_buffer_load_b128(r, 0, idx * (int)sizeof(DevTensor), 0);
+    d.d1 = __builtin_amdgcn_raw_buffer_load_b128(r, 16, idx * (int)sizeof(DevTensor), 0);
+    return d;
+}
+
+// The matrix part wave `wave` computes for item `it`: a gate/up item's 128
+// rows of gate and of up go to the two halves of the waves, a down item's 256
+// rows to all waves, kWaveRB row blocks of 16 each.
+template <int NG>
+__device__ __forceinline__ WaveJob make_job(const Params &p, const DescRaw &d, const Item &it,
+                                            int wave)
+{
+    static_assert(sizeof(DevTensor) == 32, "descriptor layout");
     WaveJob J;
-    J.codes = (gu32p)T.codes;
-    J.scales = (gu8p)T.scales;
-    J.lut = T.lut;
-    J.ts = T.tensor_scale;
-    J.bits = T.bits;
+    J.codes = (gu32p)(uintptr_t)uniform(((uint64_t)d.d0[1] << 32) | d.d0[0]);
+    J.scales = (gu8p)(uintptr_t)uniform(((uint64_t)d.d0[3] << 32) | d.d0[2]);
+    J.lut = (const uint16_t *)(uintptr_t)uniform(((uint64_t)d.d1[1] << 32) | d.d1[0]);
+    J.ts = __uint_as_float((uint32_t)uniform((int)d.d1[2]));
+    J.bits = uniform((int)d.d1[3]);
     J.G = it.down ? p.I / 128 : p.H / 128;
-    J.rb0 = it.down ? it.rb * 16 + wave * kWaveRB : it.rb * 8 + (wave & 3) * kWaveRB;
+    J.rb0 = it.down ? it.rb * 16 + wave * kWaveRB
+                    : it.rb * 8 + (wave % (kExpertWaves / 2)) * kWaveRB;
     J.g0 = it.kq * NG;
     return J;
 }
 
 struct Smem {
     int done_tok[kGroupRows];
-    int staged[2][kExpertWaves];  // per wave: next item's rows staged (by buffer)
-    int tnext[2];                 // ticket of the next item (by buffer)
     int flag;
 };
 
 // Last column split of a gate/up block: h = silu(g) * u over rows
 // rb*128..+127 of each token, then (codebook) h~ = (1/sqrt 128) H_128 (s_I h).
-// One wave per token; all partial-sum loads of a wave are issued together.
+// One wave per token; a wave issues the partial-sum loads of two tokens and
+// four splits together.
 __device__ void finish_h(const Params &p, int off, int R, int rb)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = rb * 128 + 2 * lane;
-    constexpr int TPW = kGroupRows / kExpertWaves;  // tokens per wave
-    floatx2 g[TPW], u[TPW];
+    constexpr int TPP = 2;  // tokens per pass
+    for (int t0 = wave; t0 < R; t0 += TPP * kExpertWaves) {
+        floatx2 g[TPP], u[TPP];
 #pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-        g[ti] = floatx2{0.f, 0.f};
-        u[ti] = floatx2{0.f, 0.f};
-    }
-    for (int s0 = 0; s0 < p.ks1; s0 += 4) {
-        uint64_t vg[TPW][4], vu[TPW][4];
-#pragma unroll
-        for (int ti = 0; ti < TPW; ++ti)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int tok = wave + kExpertWaves * ti;
-                vg[ti][s] = vu[ti][s] = 0;
-                if (tok < R && s0 + s < p.ks1) {
-                    const size_t row = (size_t)(s0 + s) * p.pair_cap + off + tok;
-                    vg[ti][s] = ld_coherent((const uint64_t *)(p.gu_part + (row * 2 + 0) * p.I + n));
-                    vu[ti][s] = ld_coherent((const uint64_t *)(p.gu_part + (row * 2 + 1) * p.I + n));
-                }
-            }
-#pragma unroll
-        for (int ti = 0; ti < TPW; ++ti)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                if (s0 + s < p.ks1) {
-                    g[ti] += __builtin_bit_cast(floatx2, vg[ti][s]);
-                    u[ti] += __builtin_bit_cast(floatx2, vu[ti][s]);
-                }
-    }
-#pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-        const int tok = wave + kExpertWaves * ti;
-        if (tok >= R)
-            break;
-        float v0 = g[ti][0] / (1.0f + expf(-g[ti][0])) * u[ti][0];
-        float v1 = g[ti][1] / (1.0f + expf(-g[ti][1])) * u[ti][1];
-        if (p.format == kFmtCodebook) {
-            v0 *= (float)p.signs_i[n];
-            v1 *= (float)p.signs_i[n + 1];
-            wave_fwht128(v0, v1);
-            v0 *= kInvSqrt128;
-            v1 *= kInvSqrt128;
+        for (int ti = 0; ti < TPP; ++ti) {
+            g[ti] = floatx2{0.f, 0.f};
+            u[ti] = floatx2{0.f, 0.f};
         }
-        st_coherent((uint32_t *)(p.hr + (size_t)(off + tok) * p.I + n),
-                    __builtin_bit_cast(uint32_t, half2v{(_Float16)v0, (_Float16)v1}));
+        for (int s0 = 0; s0 < p.ks1; s0 += 4) {
+            uint64_t vg[TPP][4], vu[TPP][4];
+#pragma unroll
+            for (int ti = 0; ti < TPP; ++ti)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int tok = t0 + kExpertWaves * ti;
+                    vg[ti][s] = vu[ti][s] = 0;
+                    if (tok < R && s0 + s < p.ks1) {
+                        const size_t row = (size_t)(s0 + s) * p.pair_cap + off + tok;
+                        vg[ti][s] = ld_coherent((const uint64_t *)(p.gu_part + (row * 2 + 0) * p.I + n));
+                        vu[ti][s] = ld_coherent((const uint64_t *)(p.gu_part + (row * 2 + 1) * p.I + n));
+                    }
+                }
+#pragma unroll
+            for (int ti = 0; ti < TPP; ++ti)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    if (s0 + s < p.ks1) {
+                        g[ti] += __builtin_bit_cast(floatx2, vg[ti][s]);
+                        u[ti] += __builtin_bit_cast(floatx2, vu[ti][s]);
+                    }
+        }
+#pragma unroll
+        for (int ti = 0; ti < TPP; ++ti) {
+            const int tok = t0 + kExpertWaves * ti;
+            if (tok >= R)
+                break;
+            float v0 = g[ti][0] / (1.0f + expf(-g[ti][0])) * u[ti][0];
+            float v1 = g[ti][1] / (1.0f + expf(-g[ti][1])) * u[ti][1];
+            if (p.format == kFmtCodebook) {
+                v0 *= (float)p.signs_i[n];
+                v1 *= (float)p.signs_i[n + 1];
+                wave_fwht128(v0, v1);
+                v0 *= kInvSqrt128;
+                v1 *= kInvSqrt128;
+            }
+            st_coherent((uint32_t *)(p.hr + (size_t)(off + tok) * p.I + n),
+                        __builtin_bit_cast(uint32_t, half2v{(_Float16)v0, (_Float16)v1}));
+        }
     }
 }
 
@@ -671,11 +692,12 @@ __device__ void combine_rows(const Params &p, int t, int rb)
         return;
     const int row = rb * 256 + threadIdx.x;
     float o = 0.0f;
-    for (int j0 = 0; j0 < p.k; j0 += 8) {
-        int pp[8];
-        float wj[8];
+    constexpr int SPP = 4;  // slots per pass
+    for (int j0 = 0; j0 < p.k; j0 += SPP) {
+        int pp[SPP];
+        float wj[SPP];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < SPP; ++jj) {
             pp[jj] = 0;
             wj[jj] = 0.0f;
             if (j0 + jj < p.k) {
@@ -683,14 +705,14 @@ __device__ void combine_rows(const Params &p, int t, int rb)
                 wj[jj] = p.wts[t * p.k + j0 + jj];
             }
         }
-        float y[8];
+        float y[SPP];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
+        for (int jj = 0; jj < SPP; ++jj)
             y[jj] = 0.0f;
         for (int s0 = 0; s0 < p.ks2; s0 += 2) {
-            float v[8][2];
+            float v[SPP][2];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
+            for (int jj = 0; jj < SPP; ++jj)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     v[jj][s] = 0.0f;
@@ -699,14 +721,14 @@ __device__ void combine_rows(const Params &p, int t, int rb)
                             &p.y_part[((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row]);
                 }
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
+            for (int jj = 0; jj < SPP; ++jj)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     if (s0 + s < p.ks2)
                         y[jj] += v[jj][s];
         }
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
+        for (int jj = 0; jj < SPP; ++jj)
             if (j0 + jj < p.k)
                 o += wj[jj] * y[jj];
     }
@@ -714,11 +736,16 @@ __device__ void combine_rows(const Params &p, int t, int rb)
 }
 
 // Wait until every 128-row block of h~ of row group u is written (bounded).
+// The pause between polls doubles up to about a microsecond, so waiting
+// blocks add little traffic to the counter the producers increment.
 __device__ __forceinline__ bool wait_h(const Params &p, int u)
 {
     uint32_t polls = 0;
-    while (atomic_load_agent(&p.h_ready[u]) < (uint32_t)p.n_rb1) {
-        __builtin_amdgcn_s_sleep(2);
+    int pause = 1;
+    while (atomic_load_agent(&p.h_ready[u * kCtrStride]) < (uint32_t)p.n_rb1) {
+        for (int i = 0; i < pause; ++i)
+            __builtin_amdgcn_s_sleep(4);
+        pause = min(2 * pause, 8);
         if (++polls > p.spin_limit) {
             __hip_atomic_fetch_or(&p.ctr->error_word, kErrSpinLimit, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
@@ -730,45 +757,42 @@ __device__ __forceinline__ bool wait_h(const Params &p, int u)
 
 // Staged activations of one item, R rows x KC columns of fp16: gate/up items
 // stage the rotated activations of the group's tokens (columns kq*KC..),
-// down items stage h~ of the group's rows. Each thread holds up to ITERS
-// 16-byte chunks; indices past the end are clamped to the last chunk (a
-// duplicate write of the same value).
+// down items stage h~ of the group's rows. Thread tid moves 16-byte chunks
+// tid, tid + kExpertThreads, ...; a wave skips the rounds that lie wholly past
+// the last chunk, and inside a round indices past the end are clamped to the
+// last chunk (a duplicate write of the same value).
 template <int NG>
 struct Stage {
     static constexpr int KC = NG * 128;
     static constexpr int CHUNKS = KC / 8;
     static constexpr int ITERS = (kGroupRows * CHUNKS + kExpertThreads - 1) / kExpertThreads;
     static constexpr int ASTRIDE = KC + kLdsPadHalves;   // LDS row stride (halves)
-    static constexpr int BUF = kGroupRows * ASTRIDE;      // halves per LDS buffer
-    u32x4 v[ITERS];
 
-    __device__ __forceinline__ void issue(const Params &p, const Item &it, const int *s_tok)
+    __device__ __forceinline__ static void run(const Params &p, const Item &it, const int *s_tok,
+                                               _Float16 *A)
     {
         const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
-        if (it.down) {
-            // h~ rows off..off+R-1 are consecutive: one coherent buffer
-            const _Float16 *base = p.hr + (size_t)it.off * p.I + (size_t)it.kq * KC;
+        const int wave_first = uniform(tid & ~63);
+        u32x4 v[ITERS];
 #pragma unroll
-            for (int k = 0; k < ITERS; ++k) {
-                const int i = min(tid + k * kExpertThreads, last);
-                const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+        for (int k = 0; k < ITERS; ++k) {
+            if (wave_first + k * kExpertThreads > last)
+                break;
+            const int i = min(tid + k * kExpertThreads, last);
+            const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+            if (it.down) {
+                // h~ rows off..off+R-1 are consecutive: one coherent buffer
+                const _Float16 *base = p.hr + (size_t)it.off * p.I + (size_t)it.kq * KC;
                 v[k] = ld_coherent16(base, (uint32_t)((r * p.I + c) * 2));
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < ITERS; ++k) {
-                const int i = min(tid + k * kExpertThreads, last);
-                const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+            } else {
                 const _Float16 *row = p.xr + (size_t)s_tok[it.off + r] * p.H + it.kq * KC;
                 v[k] = *(const u32x4 GLOBAL *)(row + c);
             }
         }
-    }
-    __device__ __forceinline__ void commit(const Item &it, _Float16 *A) const
-    {
-        const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
 #pragma unroll
         for (int k = 0; k < ITERS; ++k) {
+            if (wave_first + k * kExpertThreads > last)
+                break;
             const int i = min(tid + k * kExpertThreads, last);
             const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
             *(u32x4 *)(A + r * ASTRIDE + c) = v[k];
@@ -778,15 +802,12 @@ struct Stage {
 
 // Store an item's partial sums and publish them; the last split of a gate/up
 // block finishes h, the last down contribution of a (token, 256-row block)
-// combines it. `between` runs after the stores are acknowledged and before
-// the block barrier (it commits the next item's staged rows).
-template <typename Between>
+// combines it.
 __device__ __forceinline__ void finish_item(const Params &p, const Item &it, const WaveJob &J,
-                                            const floatx4 (&acc)[kWaveRB], Smem &sm,
-                                            Between &between)
+                                            const floatx4 (&acc)[kWaveRB], Smem &sm)
 {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int proj = it.down ? 2 : ((tid >> 6) >> 2);
+    const int proj = item_proj(it, tid >> 6);
 #pragma unroll
     for (int i = 0; i < kWaveRB; ++i)
 #pragma unroll
@@ -801,11 +822,10 @@ __device__ __forceinline__ void finish_item(const Params &p, const Item &it, con
             }
         }
     wait_stores();
-    between();
     __syncthreads();
     if (!it.down) {
         if (tid == 0)
-            sm.flag = atomic_add_agent(&p.rb_done[it.u * p.n_rb1 + it.rb], 1u) ==
+            sm.flag = atomic_add_agent(&p.rb_done[(it.u * p.n_rb1 + it.rb) * kCtrStride], 1u) ==
                       (uint32_t)(p.ks1 - 1);
         __syncthreads();
         if (sm.flag) {
@@ -813,13 +833,13 @@ __device__ __forceinline__ void finish_item(const Params &p, const Item &it, con
             wait_stores();
             __syncthreads();
             if (tid == 0)
-                atomic_add_agent(&p.h_ready[it.u], 1u);
+                atomic_add_agent(&p.h_ready[it.u * kCtrStride], 1u);
         }
         return;
     }
     if (tid < it.R) {
         const int t = p.rows[it.off + tid] / p.k;
-        const uint32_t old = atomic_add_agent(&p.comb[t * p.n_rb2 + it.rb], 1u);
+        const uint32_t old = atomic_add_agent(&p.comb[(t * p.n_rb2 + it.rb) * kCtrStride], 1u);
         sm.done_tok[tid] = old == (uint32_t)(p.k * p.ks2 - 1) ? t : -1;
     }
     __syncthreads();
@@ -841,143 +861,116 @@ __device__ __forceinline__ u32x4 load_lut_raw(const WaveJob &J)
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Persistent block: pulls tickets and pipelines items. Item i computes from
-// registers filled during item i-1: while it runs, the next item's codebook,
-// activation rows (into the other LDS staging buffer) and weight pairs are
-// loaded, pair p+1 as soon as pair p of item i is consumed, so every load has
-// at least one pair's compute time before the item's tail waits for it. The
-// ticket of item i+2 is claimed during item i and published at its tail.
-// Staging buffer, ticket slot and staged flags alternate between items, so
-// every value a wave reads after a barrier is written again only after the
-// next barrier.
+// Persistent block: block b takes items b, b + G, b + 2G, ... (G = grid
+// size) in order. The assignment is static: claiming items from shared
+// counters puts the blocks' atomics on a few addresses, and such atomics
+// serialize across the chip (measured slower than the static order here). No
+// wait can deadlock: every block finishes all its gate/up items (which never
+// wait) before its first down item, and every block is resident.
+// Each item stages its activation rows in LDS, then runs its 128-column
+// weight groups through two register buffers; the buffers freed by the
+// item's last two groups already receive the next item's first two groups
+// (and its codebook), so those loads overlap the end of the item, its tail
+// and the next item's staging. Four waves per SIMD (four blocks per CU, the
+// 128-register budget): other blocks' groups cover each block's staging and
+// tail latencies.
 template <int CLASS, int NG>
-__global__ __launch_bounds__(kExpertThreads) void expert_kernel(Params p)
+__global__ __launch_bounds__(kExpertThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void expert_kernel(Params p)
 {
-    extern __shared__ _Float16 Abuf[];  // two staging buffers of min(m, 16) rows
+    extern __shared__ _Float16 Abuf[];  // min(m, 16) staged rows
     __shared__ Smem sm;
     __shared__ int s_tok[kMaxPairs];    // token of each bucket row
-    constexpr bool TWO = NG > 1;
-    constexpr int NP = kPairs<NG>;
+    __shared__ GroupLds s_grp;
     using St = Stage<NG>;
     const Plan *P = p.plan;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = uniform(tid >> 6);
     const int r16 = lane & 15, q = lane >> 4;
-    const int buf_halves = min(P->m, kGroupRows) * St::ASTRIDE;
+    const int m = uniform(P->m), n_items = uniform(P->n_items), n_items1 = uniform(P->n_items1);
+    const int n_groups = uniform(P->n_groups);
 
-    for (int i = tid; i < P->m * p.k; i += kExpertThreads)
+    for (int i = tid; i < m * p.k; i += kExpertThreads)
         s_tok[i] = p.rows[i] / p.k;
-    if (tid == 0)
-        sm.tnext[0] = (int)gridDim.x + (int)atomic_add_agent(&p.ctr->ticket, 1u);
+    for (int i = tid; i < n_groups; i += kExpertThreads) {
+        s_grp.expert[i] = P->g_expert[i];
+        s_grp.off[i] = P->g_off[i];
+        s_grp.rows[i] = P->g_rows[i];
+    }
     __syncthreads();
 
-    Item cur = make_item(p, P, blockIdx.x);
+    int ticket = blockIdx.x;
+    Item cur = make_item(p, n_items, n_items1, s_grp, ticket);
     uint32_t done = 0;
     if (cur.valid) {
-        int buf = 0;
-        PairBuf<CLASS> b[NP];
-        St st;
-        WaveJob J = make_job<NG>(p, cur, wave);
+        GroupBuf<CLASS> bA, bB;
+        WaveJob J = make_job<NG>(p, load_desc(p, cur, wave), cur, wave);
         int sc_lane = CLASS == kFmtCodebook ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
         u32x4 lut = u32x4{0, 0, 0, 0};
-        // first item: nothing was prefetched
-        bool ok = true;
-        if (cur.down) {
-            if (tid == 0)
-                sm.flag = wait_h(p, cur.u);
-            __syncthreads();
-            ok = sm.flag != 0;
-        }
-        st.issue(p, cur, s_tok);
         if constexpr (CLASS == kFmtCodebook)
             lut = load_lut_raw(J);
-#pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
-            load_pair<CLASS, TWO, 0>(b[pp], J, pp, lane, sc_lane);
-        st.commit(cur, Abuf);
-        __syncthreads();
+        load_group<CLASS, 0>(bA, J, 0, lane, sc_lane);
+        if constexpr (NG > 1)
+            load_group<CLASS, 0>(bB, J, 1, lane, sc_lane);
 
         while (true) {
-            uint32_t t_after = 0;
-            if (tid == 0)
-                t_after = gridDim.x + atomic_add_agent(&p.ctr->ticket, 1u);
-            const Item nxt = make_item(p, P, uniform(sm.tnext[buf]));
-            WaveJob JN{};
-            if (nxt.valid)
-                JN = make_job<NG>(p, nxt, wave);
-            const int sc_next = CLASS == kFmtCodebook ? r16 * JN.G * 2 : r16 * JN.G * 8 + 2 * q;
+            // the next item's plan entries (LDS) and descriptor (vector loads)
+            const int nxt_ticket = ticket + (int)gridDim.x;
+            const Item nxt = make_item(p, n_items, n_items1, s_grp, nxt_ticket);
+            const DescRaw dn = load_desc(p, nxt, wave);
+
+            // this item's activation rows: a down item's rows once its h is
+            // complete (bounded wait)
+            bool ok = true;
+            if (cur.down) {
+                if (tid == 0)
+                    sm.flag = wait_h(p, cur.u);
+                __syncthreads();
+                ok = sm.flag != 0;
+            }
+            St::run(p, cur, s_tok, Abuf);
+            __syncthreads();
+
             uint32_t tab[4] = {0, 0, 0, 0};
             if constexpr (CLASS == kFmtCodebook)
                 lut_tables(lut, tab);
-
-            // next item, first part: its rows of activations (a down item's
-            // rows only once its h is complete), its codebook, its first pair
-            bool staged = false;
-            PairBuf<CLASS> nb[NP];
-            if (nxt.valid) {
-                staged = !nxt.down ||
-                         (uint32_t)uniform((int)atomic_load_agent(&p.h_ready[nxt.u])) >=
-                             (uint32_t)p.n_rb1;
-                if (staged)
-                    st.issue(p, nxt, s_tok);
-                if constexpr (CLASS == kFmtCodebook)
-                    lut = load_lut_raw(JN);
-                load_pair<CLASS, TWO, 0>(nb[0], JN, 0, lane, sc_next);
-            }
-            auto after = [&](int pp) {
-                if (nxt.valid && pp + 1 < NP)
-                    load_pair<CLASS, TWO, 0>(nb[pp + 1], JN, pp + 1, lane, sc_next);
+            WaveJob JN{};
+            int sc_next = 0;
+            // after group j, the freed buffer takes this item's group j+2,
+            // else the next item's group j+2-NG (a single-group item reuses
+            // its one buffer for the next item's group 0)
+            auto after = [&](int j, GroupBuf<CLASS> &b) {
+                const int nx = NG == 1 ? 0 : j + 2 - NG;
+                if (NG > 1 && j + 2 < NG) {
+                    load_group<CLASS, 0>(b, J, j + 2, lane, sc_lane);
+                } else if (nxt.valid && nx >= 0) {
+                    if (nx == 0) {
+                        JN = make_job<NG>(p, dn, nxt, wave);
+                        sc_next = CLASS == kFmtCodebook ? r16 * JN.G * 2 : r16 * JN.G * 8 + 2 * q;
+                        if constexpr (CLASS == kFmtCodebook)
+                            lut = load_lut_raw(JN);
+                    }
+                    load_group<CLASS, 0>(b, JN, nx, lane, sc_next);
+                }
             };
-            const _Float16 *Arow = Abuf + buf * buf_halves + min(r16, cur.R - 1) * St::ASTRIDE + q * 32;
+            const _Float16 *Arow = Abuf + min(r16, cur.R - 1) * St::ASTRIDE + q * 32;
             floatx4 acc[kWaveRB];
-            compute_item<CLASS, NG>(b, J.bits, J.ts, Arow, tab, acc, after);
+            compute_item<CLASS, NG>(bA, bB, J.bits, J.ts, Arow, tab, acc, after);
 
-            auto between = [&]() {
-                if (staged)
-                    st.commit(nxt, Abuf + (buf ^ 1) * buf_halves);
-                if (lane == 0)
-                    sm.staged[buf ^ 1][wave] = staged;
-                if (tid == 0)
-                    sm.tnext[buf ^ 1] = (int)t_after;
-            };
-            if (ok) {
-                finish_item(p, cur, J, acc, sm, between);
-            } else {
-                between();
-            }
+            if (ok)
+                finish_item(p, cur, J, acc, sm);
             ++done;
             __syncthreads();
             if (!nxt.valid)
                 break;
-            buf ^= 1;
-            bool all_staged = true;
-#pragma unroll
-            for (int w = 0; w < kExpertWaves; ++w)
-                all_staged = all_staged && sm.staged[buf][w] != 0;
+            ticket = nxt_ticket;
             cur = nxt;
             J = JN;
             sc_lane = sc_next;
-#pragma unroll
-            for (int pp = 0; pp < NP; ++pp)
-                b[pp] = nb[pp];
-            ok = true;
-            if (!all_staged) {
-                // some wave could not stage its share of the rows (h not yet
-                // complete when it looked): wait and stage them all now
-                if (cur.down) {
-                    if (tid == 0)
-                        sm.flag = wait_h(p, cur.u);
-                    __syncthreads();
-                    ok = sm.flag != 0;
-                }
-                st.issue(p, cur, s_tok);
-                st.commit(cur, Abuf + buf * buf_halves);
-                __syncthreads();
-            }
         }
     }
     if (tid == 0 && done)
-        atomic_add_agent(&p.ctr->items_done, done);
+        atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], done);
 }
 
 // ---------------------------------------------------------------------------

@@ -160,7 +160,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.n_rb1 = p.I / 128;
     p.n_rb2 = p.H / 256;
     p.pair_cap = p.max_tokens * p.k;
-    p.spin_limit = 20u * 1000u * 1000u;
+    p.spin_limit = 2u * 1000u * 1000u;  // polls of up to ~1 us: a ~2 s bound
     p.signs_h = cfg->signs_hidden;
     p.signs_i = cfg->signs_inter;
     h->max_tokens = cfg->max_tokens;
@@ -192,8 +192,9 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     const size_t o_ids = take(4 * PC), o_wts = take(4 * PC), o_counts = take(4 * E),
                  o_offsets = take(4 * (E + 1)), o_rows = take(4 * PC), o_pos = take(4 * PC);
     const size_t o_plan = take(sizeof(Plan));
-    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(4 * kMaxGroups * p.n_rb1),
-                 o_hready = take(4 * kMaxGroups), o_comb = take(4 * M * p.n_rb2);
+    const size_t ctr_b = 4 * kCtrStride;  // one counter per 128-byte line
+    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(ctr_b * kMaxGroups * p.n_rb1),
+                 o_hready = take(ctr_b * kMaxGroups), o_comb = take(ctr_b * M * p.n_rb2);
     const size_t ctr_end = off;
     const size_t o_xr = take(2 * M * H), o_gu = take(4 * (size_t)p.ks1 * PC * 2 * I),
                  o_hr = take(2 * PC * I), o_y = take(4 * (size_t)p.ks2 * PC * H);
@@ -239,8 +240,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     h->bpc.assign(M + 1, 0);
     h->lds.assign(M + 1, 0);
     for (int m = 1; m <= (int)M; ++m) {
-        // two staging buffers (the next item's rows load while this one computes)
-        const size_t lds = 2 * (size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) * sizeof(_Float16);
+        const size_t lds = (size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) * sizeof(_Float16);
         int bpc = 0;
         err = expert_occupancy(p.format, p.kc1 / 128, &bpc, lds);
         if (err != hipSuccess || bpc < 1)
@@ -354,7 +354,10 @@ extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_
         st.m = plan.m;
         st.hit_experts = plan.n_hit;
         st.items = plan.n_items;
-        st.items_done = (int32_t)c.items_done;
+        uint32_t done = 0;
+        for (int i = 0; i < kDoneSlots; ++i)
+            done += c.items_done[i];
+        st.items_done = (int32_t)done;
         st.error_word = (int32_t)c.error_word;
         memcpy(dst, &st, sizeof st);
     }

@@ -19,6 +19,11 @@ constexpr int kLdsPadHalves = 8;    // 16 B row padding of the staged activation
 constexpr int kFmtCodebook = 1;
 constexpr int kFmtNvfp4 = 2;
 
+// Cross-block counters (rb_done, h_ready, comb) sit one per 128-byte line:
+// blocks polling one counter must not queue behind traffic to its
+// neighbours, as they would when packed.
+constexpr int kCtrStride = 32;  // uint32 per counter slot
+
 // Error bits of Counters::error_word.
 constexpr uint32_t kErrSpinLimit = 1u;
 
@@ -44,11 +49,14 @@ struct Plan {
     int32_t g_rows[kMaxGroups];    // rows of u (1..16)
 };
 
+// Completed work items are counted on kDoneSlots counters (block b adds to
+// slot b % kDoneSlots) so that no single address takes every block's atomic.
+constexpr int kDoneSlots = 8;
+
 struct Counters {
-    uint32_t ticket;       // dynamic work-item tickets handed out
-    uint32_t items_done;   // work items completed (statistics)
-    uint32_t error_word;   // kErr* bits
-    uint32_t pad[5];
+    uint32_t items_done[kDoneSlots];  // work items completed (statistics)
+    uint32_t error_word;              // kErr* bits
+    uint32_t pad[7];
 };
 
 // Everything a kernel needs, passed by value.
@@ -79,6 +87,7 @@ struct Params {
     uint32_t *rb_done;     // [kMaxGroups][n_rb1] finished column splits per row block
     uint32_t *h_ready;     // [kMaxGroups] finished row blocks of h per row group
     uint32_t *comb;        // [max_tokens][n_rb2] finished down contributions per token block
+                           // (all three: one counter per kCtrStride uint32)
 };
 
 // Kernel launchers (kernels.hip).
