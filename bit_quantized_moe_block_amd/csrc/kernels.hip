@@ -256,7 +256,7 @@ __device__ void route_block(const Params &p, const float *__restrict__ logits, i
     }
     if (tid == 0) {
         p.offsets[E] = total;
-        const int n1 = ngroups * p.n_rb1 * p.ks1;
+        const int n1 = ngroups * (p.n_rb1 / p.span1) * p.ks1;
         P->m = m;
         P->n_hit = nhit;
         P->n_groups = ngroups;
@@ -270,8 +270,6 @@ __device__ void route_block(const Params &p, const float *__restrict__ logits, i
         p.rb_done[i * kCtrStride] = 0;
     for (int i = tid; i < ngroups; i += kRouteThreads)
         p.h_ready[i * kCtrStride] = 0;
-    for (int i = tid; i < m * p.n_rb2; i += kRouteThreads)
-        p.comb[i * kCtrStride] = 0;
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
@@ -512,29 +510,21 @@ __device__ __forceinline__ void process_any(const GroupBuf<CLASS> &b, int j, int
     }
 }
 
-// All NG groups of the current item from two register buffers used in turn.
-// `after(j, buf)` runs once group j is consumed, with the buffer that held
-// it: it loads what that buffer holds next (group j+2 of this item, or one
-// of the next item's first two groups).
+// The NG groups of the current chunk from two register buffers used in turn,
+// accumulated into acc. `after(j, buf)` runs once group j is consumed, with
+// the buffer that held it: it loads what that buffer holds next (group j+2 of
+// this chunk, or one of the first two groups of the next chunk or item).
 template <int CLASS, int NG, typename After>
-__device__ __forceinline__ void compute_item(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
-                                             float ts, const _Float16 *Arow,
-                                             const uint32_t (&tab)[4], floatx4 (&acc)[kWaveRB],
-                                             After &after)
+__device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
+                                              const _Float16 *Arow, const uint32_t (&tab)[4],
+                                              floatx4 (&acc)[kWaveRB], After &after)
 {
-#pragma unroll
-    for (int i = 0; i < kWaveRB; ++i)
-        acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         GroupBuf<CLASS> &b = (j & 1) ? bB : bA;
         process_any<CLASS>(b, j, bits, Arow, tab, acc);
         after(j, b);
     }
-    if constexpr (CLASS != kFmtCodebook)
-#pragma unroll
-        for (int i = 0; i < kWaveRB; ++i)
-            acc[i] *= ts;
 }
 
 // ---------------------------------------------------------------------------
@@ -544,8 +534,11 @@ __device__ __forceinline__ void compute_item(GroupBuf<CLASS> &bA, GroupBuf<CLASS
 // One work item: gate/up (row group u = expert e's rows off..off+R-1, 128-row
 // block rb of gate and up, column split kq) or down (256-row block rb of
 // down, column split kq).
+// Work item: row group u (expert e, bucket rows off..off+R-1), column split
+// kq, `span` consecutive row blocks from rb (128 rows each for gate/up, 256
+// rows for down).
 struct Item {
-    int valid, down, e, off, R, u, rb, kq;
+    int valid, down, e, off, R, u, rb, kq, span;
 };
 
 // Row-group table of the plan, cached in LDS by every block: expert, first
@@ -564,11 +557,13 @@ __device__ __forceinline__ Item make_item(const Params &p, int n_items, int n_it
     it.down = ticket >= n_items1;
     const int t = it.down ? ticket - n_items1 : ticket;
     const int ks = it.down ? p.ks2 : p.ks1;
-    const int per_u = (it.down ? p.n_rb2 : p.n_rb1) * ks;
+    it.span = it.down ? 1 : p.span1;
+    const int per_u = (it.down ? p.n_rb2 : p.n_rb1 / p.span1) * ks;
     it.u = t / per_u;
     const int rem = t - it.u * per_u;
-    it.rb = rem / ks;
-    it.kq = rem - it.rb * ks;
+    const int rbs = rem / ks;
+    it.rb = rbs * it.span;
+    it.kq = rem - rbs * ks;
     it.e = uniform(gl.expert[it.u]);
     it.off = uniform(gl.off[it.u]);
     it.R = uniform(gl.rows[it.u]);
@@ -621,9 +616,11 @@ __device__ __forceinline__ WaveJob make_job(const Params &p, const DescRaw &d, c
     return J;
 }
 
+constexpr int kMaxSpan = 2;  // row blocks per gate/up item
+
 struct Smem {
-    int done_tok[kGroupRows];
     int flag;
+    int last[kMaxSpan];  // this item's split was the last of row block rb + s
 };
 
 // Last column split of a gate/up block: h = silu(g) * u over rows
@@ -685,56 +682,6 @@ __device__ void finish_h(const Params &p, int off, int R, int rb)
     }
 }
 
-// out[t][rb*256 + tid] = sum_j w[t][j] * sum_s y_part[s][pos(t, j)], slot order.
-__device__ void combine_rows(const Params &p, int t, int rb)
-{
-    if (threadIdx.x >= 256)
-        return;
-    const int row = rb * 256 + threadIdx.x;
-    float o = 0.0f;
-    constexpr int SPP = 4;  // slots per pass
-    for (int j0 = 0; j0 < p.k; j0 += SPP) {
-        int pp[SPP];
-        float wj[SPP];
-#pragma unroll
-        for (int jj = 0; jj < SPP; ++jj) {
-            pp[jj] = 0;
-            wj[jj] = 0.0f;
-            if (j0 + jj < p.k) {
-                pp[jj] = p.pos[t * p.k + j0 + jj];
-                wj[jj] = p.wts[t * p.k + j0 + jj];
-            }
-        }
-        float y[SPP];
-#pragma unroll
-        for (int jj = 0; jj < SPP; ++jj)
-            y[jj] = 0.0f;
-        for (int s0 = 0; s0 < p.ks2; s0 += 2) {
-            float v[SPP][2];
-#pragma unroll
-            for (int jj = 0; jj < SPP; ++jj)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    v[jj][s] = 0.0f;
-                    if (j0 + jj < p.k && s0 + s < p.ks2)
-                        v[jj][s] = ld_coherent(
-                            &p.y_part[((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row]);
-                }
-#pragma unroll
-            for (int jj = 0; jj < SPP; ++jj)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    if (s0 + s < p.ks2)
-                        y[jj] += v[jj][s];
-        }
-#pragma unroll
-        for (int jj = 0; jj < SPP; ++jj)
-            if (j0 + jj < p.k)
-                o += wj[jj] * y[jj];
-    }
-    p.out[(size_t)t * p.H + row] = o;
-}
-
 // Wait until every 128-row block of h~ of row group u is written (bounded).
 // The pause between polls doubles up to about a microsecond, so waiting
 // blocks add little traffic to the counter the producers increment.
@@ -755,56 +702,64 @@ __device__ __forceinline__ bool wait_h(const Params &p, int u)
     return true;
 }
 
-// Staged activations of one item, R rows x KC columns of fp16: gate/up items
-// stage the rotated activations of the group's tokens (columns kq*KC..),
-// down items stage h~ of the group's rows. Thread tid moves 16-byte chunks
+// Staged activations of one item, R rows x KC columns of fp16:
+// gate/up items stage the rotated activations of the group's tokens, down
+// items stage h~ of the group's rows. Thread tid moves 16-byte chunks
 // tid, tid + kExpertThreads, ...; a wave skips the rounds that lie wholly past
 // the last chunk, and inside a round indices past the end are clamped to the
-// last chunk (a duplicate write of the same value).
+// last chunk (a duplicate write of the same value). issue() starts the loads,
+// commit() writes them to LDS once they are needed: loads issued in between
+// (the chunk's first weight groups) stay in flight.
 template <int NG>
 struct Stage {
     static constexpr int KC = NG * 128;
     static constexpr int CHUNKS = KC / 8;
     static constexpr int ITERS = (kGroupRows * CHUNKS + kExpertThreads - 1) / kExpertThreads;
     static constexpr int ASTRIDE = KC + kLdsPadHalves;   // LDS row stride (halves)
+    u32x4 v[ITERS];
 
-    __device__ __forceinline__ static void run(const Params &p, const Item &it, const int *s_tok,
-                                               _Float16 *A)
+    __device__ __forceinline__ void issue(const Params &p, const Item &it, const int *s_tok)
     {
         const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
         const int wave_first = uniform(tid & ~63);
-        u32x4 v[ITERS];
+        const int col0 = it.kq * KC;
 #pragma unroll
         for (int k = 0; k < ITERS; ++k) {
+            v[k] = u32x4{0, 0, 0, 0};
             if (wave_first + k * kExpertThreads > last)
-                break;
+                continue;
             const int i = min(tid + k * kExpertThreads, last);
-            const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
+            const int r = i / CHUNKS, cc = (i - r * CHUNKS) * 8;
             if (it.down) {
                 // h~ rows off..off+R-1 are consecutive: one coherent buffer
-                const _Float16 *base = p.hr + (size_t)it.off * p.I + (size_t)it.kq * KC;
-                v[k] = ld_coherent16(base, (uint32_t)((r * p.I + c) * 2));
+                const _Float16 *base = p.hr + (size_t)it.off * p.I + col0;
+                v[k] = ld_coherent16(base, (uint32_t)((r * p.I + cc) * 2));
             } else {
-                const _Float16 *row = p.xr + (size_t)s_tok[it.off + r] * p.H + it.kq * KC;
-                v[k] = *(const u32x4 GLOBAL *)(row + c);
+                const _Float16 *row = p.xr + (size_t)s_tok[it.off + r] * p.H + col0;
+                v[k] = *(const u32x4 GLOBAL *)(row + cc);
             }
         }
+    }
+    __device__ __forceinline__ void commit(const Item &it, _Float16 *A) const
+    {
+        const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
+        const int wave_first = uniform(tid & ~63);
 #pragma unroll
         for (int k = 0; k < ITERS; ++k) {
             if (wave_first + k * kExpertThreads > last)
-                break;
+                continue;
             const int i = min(tid + k * kExpertThreads, last);
-            const int r = i / CHUNKS, c = (i - r * CHUNKS) * 8;
-            *(u32x4 *)(A + r * ASTRIDE + c) = v[k];
+            const int r = i / CHUNKS, cc = (i - r * CHUNKS) * 8;
+            *(u32x4 *)(A + r * ASTRIDE + cc) = v[k];
         }
     }
 };
 
-// Store an item's partial sums and publish them; the last split of a gate/up
-// block finishes h, the last down contribution of a (token, 256-row block)
-// combines it.
-__device__ __forceinline__ void finish_item(const Params &p, const Item &it, const WaveJob &J,
-                                            const floatx4 (&acc)[kWaveRB], Smem &sm)
+// Store the partial sums of one row block of an item (rows rb0.. of job J).
+// Gate/up partials go out agent-coherent for the finishing block; down
+// partials are read only by the combine kernel, after this kernel ends.
+__device__ __forceinline__ void store_rows(const Params &p, const Item &it, const WaveJob &J,
+                                           const floatx4 (&acc)[kWaveRB])
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int proj = item_proj(it, tid >> 6);
@@ -816,36 +771,40 @@ __device__ __forceinline__ void finish_item(const Params &p, const Item &it, con
             if (tok < it.R) {
                 const size_t row = (size_t)it.kq * p.pair_cap + it.off + tok;
                 const int n = (J.rb0 + i) * 16 + (lane & 15);
-                float *dst = it.down ? &p.y_part[row * p.H + n]
-                                     : &p.gu_part[(row * 2 + proj) * p.I + n];
-                st_coherent(dst, acc[i][j]);
+                if (it.down)
+                    p.y_part[row * p.H + n] = acc[i][j];
+                else
+                    st_coherent(&p.gu_part[(row * 2 + proj) * p.I + n], acc[i][j]);
             }
         }
+}
+
+// After a gate/up item's stores: once they are acknowledged, count the item's
+// split in each of its row blocks; the last split of a row block finishes
+// that block of h, and the group's h counter goes up by the blocks finished.
+__device__ __forceinline__ void complete_item(const Params &p, const Item &it, Smem &sm)
+{
+    const int tid = threadIdx.x;
+    if (it.down)
+        return;
     wait_stores();
     __syncthreads();
-    if (!it.down) {
-        if (tid == 0)
-            sm.flag = atomic_add_agent(&p.rb_done[(it.u * p.n_rb1 + it.rb) * kCtrStride], 1u) ==
-                      (uint32_t)(p.ks1 - 1);
-        __syncthreads();
-        if (sm.flag) {
-            finish_h(p, it.off, it.R, it.rb);
-            wait_stores();
-            __syncthreads();
-            if (tid == 0)
-                atomic_add_agent(&p.h_ready[it.u * kCtrStride], 1u);
-        }
-        return;
-    }
-    if (tid < it.R) {
-        const int t = p.rows[it.off + tid] / p.k;
-        const uint32_t old = atomic_add_agent(&p.comb[(t * p.n_rb2 + it.rb) * kCtrStride], 1u);
-        sm.done_tok[tid] = old == (uint32_t)(p.k * p.ks2 - 1) ? t : -1;
-    }
+    if (tid < it.span)
+        sm.last[tid] = atomic_add_agent(&p.rb_done[(it.u * p.n_rb1 + it.rb + tid) * kCtrStride],
+                                        1u) == (uint32_t)(p.ks1 - 1);
     __syncthreads();
-    for (int tok = 0; tok < it.R; ++tok)
-        if (sm.done_tok[tok] >= 0)
-            combine_rows(p, sm.done_tok[tok], it.rb);
+    int finished = 0;
+    for (int s = 0; s < it.span; ++s)
+        if (sm.last[s]) {
+            finish_h(p, it.off, it.R, it.rb + s);
+            ++finished;
+        }
+    if (finished) {
+        wait_stores();
+        __syncthreads();
+        if (tid == 0)
+            atomic_add_agent(&p.h_ready[it.u * kCtrStride], (uint32_t)finished);
+    }
 }
 
 // The codebook of job J as stored, read through a buffer resource whose size
@@ -867,11 +826,14 @@ __device__ __forceinline__ u32x4 load_lut_raw(const WaveJob &J)
 // serialize across the chip (measured slower than the static order here). No
 // wait can deadlock: every block finishes all its gate/up items (which never
 // wait) before its first down item, and every block is resident.
-// Each item stages its activation rows in LDS, then runs its 128-column
-// weight groups through two register buffers; the buffers freed by the
-// item's last two groups already receive the next item's first two groups
-// (and its codebook), so those loads overlap the end of the item, its tail
-// and the next item's staging. Four waves per SIMD (four blocks per CU, the
+// An item stages its activation rows in LDS once, then for each row block of
+// its span runs the 128-column weight groups through two register buffers,
+// two groups in flight, the next row block's first groups loaded as the
+// current one ends (same activations: no barrier in between). Nothing is
+// prefetched across an item boundary: vector memory counters retire in order,
+// so a load issued before the boundary would hold up the staging and the
+// tail's store acknowledgements behind it. Instead the staging loads go first
+// and the item's first weight groups right behind them. Four waves per SIMD (four blocks per CU, the
 // 128-register budget): other blocks' groups cover each block's staging and
 // tail latencies.
 template <int CLASS, int NG>
@@ -904,73 +866,141 @@ void expert_kernel(Params p)
     uint32_t done = 0;
     if (cur.valid) {
         GroupBuf<CLASS> bA, bB;
+        int sb = 0;  // row block of cur's span being computed
         WaveJob J = make_job<NG>(p, load_desc(p, cur, wave), cur, wave);
-        int sc_lane = CLASS == kFmtCodebook ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
-        u32x4 lut = u32x4{0, 0, 0, 0};
-        if constexpr (CLASS == kFmtCodebook)
-            lut = load_lut_raw(J);
-        load_group<CLASS, 0>(bA, J, 0, lane, sc_lane);
-        if constexpr (NG > 1)
-            load_group<CLASS, 0>(bB, J, 1, lane, sc_lane);
+        uint32_t tab[4] = {0, 0, 0, 0};
 
         while (true) {
-            // the next item's plan entries (LDS) and descriptor (vector loads)
+            const bool last = sb + 1 == cur.span;
+            const int sc_lane = CLASS == kFmtCodebook ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+            // after the item's last row block comes the next item: its plan
+            // entries (LDS) and descriptor (vector loads)
             const int nxt_ticket = ticket + (int)gridDim.x;
-            const Item nxt = make_item(p, n_items, n_items1, s_grp, nxt_ticket);
+            const Item nxt = make_item(p, n_items, n_items1, s_grp, last ? nxt_ticket : n_items);
             const DescRaw dn = load_desc(p, nxt, wave);
 
-            // this item's activation rows: a down item's rows once its h is
-            // complete (bounded wait)
             bool ok = true;
-            if (cur.down) {
-                if (tid == 0)
-                    sm.flag = wait_h(p, cur.u);
+            if (sb == 0) {
+                // the item's activation rows (a down item's rows once its h is
+                // complete, bounded wait), then its codebook and first weight
+                // group; only the rows are waited on before the LDS commit,
+                // and the second group follows it
+                if (cur.down) {
+                    if (tid == 0)
+                        sm.flag = wait_h(p, cur.u);
+                    __syncthreads();
+                    ok = sm.flag != 0;
+                }
+                St st;
+                st.issue(p, cur, s_tok);
+                u32x4 lut = u32x4{0, 0, 0, 0};
+                if constexpr (CLASS == kFmtCodebook)
+                    lut = load_lut_raw(J);
+                load_group<CLASS, 0>(bA, J, 0, lane, sc_lane);
+                st.commit(cur, Abuf);
+                if constexpr (NG > 1)
+                    load_group<CLASS, 0>(bB, J, 1, lane, sc_lane);
                 __syncthreads();
-                ok = sm.flag != 0;
+                if constexpr (CLASS == kFmtCodebook)
+                    lut_tables(lut, tab);
             }
-            St::run(p, cur, s_tok, Abuf);
-            __syncthreads();
-
-            uint32_t tab[4] = {0, 0, 0, 0};
-            if constexpr (CLASS == kFmtCodebook)
-                lut_tables(lut, tab);
-            WaveJob JN{};
-            int sc_next = 0;
-            // after group j, the freed buffer takes this item's group j+2,
-            // else the next item's group j+2-NG (a single-group item reuses
-            // its one buffer for the next item's group 0)
+            // after group j, the freed buffer takes this row block's group
+            // j+2, else group j+2-NG of the span's next row block (same
+            // activations and tensor: no staging in between)
+            WaveJob JN = J;
+            JN.rb0 += (cur.down ? 16 : 8);
             auto after = [&](int j, GroupBuf<CLASS> &b) {
                 const int nx = NG == 1 ? 0 : j + 2 - NG;
-                if (NG > 1 && j + 2 < NG) {
+                if (NG > 1 && j + 2 < NG)
                     load_group<CLASS, 0>(b, J, j + 2, lane, sc_lane);
-                } else if (nxt.valid && nx >= 0) {
-                    if (nx == 0) {
-                        JN = make_job<NG>(p, dn, nxt, wave);
-                        sc_next = CLASS == kFmtCodebook ? r16 * JN.G * 2 : r16 * JN.G * 8 + 2 * q;
-                        if constexpr (CLASS == kFmtCodebook)
-                            lut = load_lut_raw(JN);
-                    }
-                    load_group<CLASS, 0>(b, JN, nx, lane, sc_next);
-                }
+                else if (!last && nx >= 0)
+                    load_group<CLASS, 0>(b, JN, nx, lane, sc_lane);
             };
             const _Float16 *Arow = Abuf + min(r16, cur.R - 1) * St::ASTRIDE + q * 32;
             floatx4 acc[kWaveRB];
-            compute_item<CLASS, NG>(bA, bB, J.bits, J.ts, Arow, tab, acc, after);
-
+#pragma unroll
+            for (int i = 0; i < kWaveRB; ++i)
+                acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, acc, after);
+            if constexpr (CLASS != kFmtCodebook)
+#pragma unroll
+                for (int i = 0; i < kWaveRB; ++i)
+                    acc[i] *= J.ts;
             if (ok)
-                finish_item(p, cur, J, acc, sm);
+                store_rows(p, cur, J, acc);
+            if (!last) {
+                ++sb;
+                J = JN;
+                continue;
+            }
+            if (ok)
+                complete_item(p, cur, sm);
             ++done;
             __syncthreads();
             if (!nxt.valid)
                 break;
             ticket = nxt_ticket;
             cur = nxt;
-            J = JN;
-            sc_lane = sc_next;
+            sb = 0;
+            J = make_job<NG>(p, dn, nxt, wave);
         }
     }
     if (tid == 0 && done)
         atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], done);
+}
+
+// ---------------------------------------------------------------------------
+// Combine
+// ---------------------------------------------------------------------------
+
+// out[t][n] = sum_j w[t][j] * sum_s y_part[s][pos(t, j)][n], slots j in
+// order, splits s in order (no float atomics: bitwise reproducible). Block
+// (rb, t) covers rows rb*256 .. +255 of token t; runs after the expert
+// kernel, so plain loads see its partial sums.
+__global__ __launch_bounds__(256) void combine_kernel(Params p)
+{
+    const int t = blockIdx.y, row = blockIdx.x * 256 + threadIdx.x;
+    constexpr int SPP = 4;  // slots per pass
+    float o = 0.0f;
+    for (int j0 = 0; j0 < p.k; j0 += SPP) {
+        int pp[SPP];
+        float wj[SPP];
+#pragma unroll
+        for (int jj = 0; jj < SPP; ++jj) {
+            pp[jj] = 0;
+            wj[jj] = 0.0f;
+            if (j0 + jj < p.k) {
+                pp[jj] = p.pos[t * p.k + j0 + jj];
+                wj[jj] = p.wts[t * p.k + j0 + jj];
+            }
+        }
+        float y[SPP];
+#pragma unroll
+        for (int jj = 0; jj < SPP; ++jj)
+            y[jj] = 0.0f;
+        for (int s0 = 0; s0 < p.ks2; s0 += 2) {
+            float v[SPP][2];
+#pragma unroll
+            for (int jj = 0; jj < SPP; ++jj)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    v[jj][s] = 0.0f;
+                    if (j0 + jj < p.k && s0 + s < p.ks2)
+                        v[jj][s] = p.y_part[((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row];
+                }
+#pragma unroll
+            for (int jj = 0; jj < SPP; ++jj)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s0 + s < p.ks2)
+                        y[jj] += v[jj][s];
+        }
+#pragma unroll
+        for (int jj = 0; jj < SPP; ++jj)
+            if (j0 + jj < p.k)
+                o += wj[jj] * y[jj];
+    }
+    p.out[(size_t)t * p.H + row] = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -1010,6 +1040,12 @@ static void *expert_kernel_for(int format, int ng)
     case 2: return expert_fn<kFmtNvfp4, 2>();
     default: return expert_fn<kFmtNvfp4, 1>();
     }
+}
+
+hipError_t launch_combine(const Params &p, int m, hipStream_t s)
+{
+    combine_kernel<<<dim3(p.n_rb2, m), dim3(256), 0, s>>>(p);
+    return hipGetLastError();
 }
 
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s)

@@ -32,6 +32,7 @@ struct moe_decode_s {
     std::vector<int> grid;       // [m] persistent grid of the expert kernel
     std::vector<int> bpc;        // [m] resident blocks per CU
     std::vector<size_t> lds;     // [m] dynamic LDS bytes
+    std::vector<int> span1;      // [m] 128-row blocks per gate/up item
     bool bound = false;
     hipStream_t stream = nullptr;
     bool ran = false;
@@ -157,6 +158,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.kc1 = p.kc2 = split_cols(p.H, p.I);
     p.ks1 = p.H / p.kc1;
     p.ks2 = p.I / p.kc2;
+    p.span1 = 1;
     p.n_rb1 = p.I / 128;
     p.n_rb2 = p.H / 256;
     p.pair_cap = p.max_tokens * p.k;
@@ -194,7 +196,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     const size_t o_plan = take(sizeof(Plan));
     const size_t ctr_b = 4 * kCtrStride;  // one counter per 128-byte line
     const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(ctr_b * kMaxGroups * p.n_rb1),
-                 o_hready = take(ctr_b * kMaxGroups), o_comb = take(ctr_b * M * p.n_rb2);
+                 o_hready = take(ctr_b * kMaxGroups);
     const size_t ctr_end = off;
     const size_t o_xr = take(2 * M * H), o_gu = take(4 * (size_t)p.ks1 * PC * 2 * I),
                  o_hr = take(2 * PC * I), o_y = take(4 * (size_t)p.ks2 * PC * H);
@@ -215,7 +217,6 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.ctr = (Counters *)(base + o_ctr);
     p.rb_done = (uint32_t *)(base + o_rbdone);
     p.h_ready = (uint32_t *)(base + o_hready);
-    p.comb = (uint32_t *)(base + o_comb);
     p.xr = (_Float16 *)(base + o_xr);
     p.gu_part = (float *)(base + o_gu);
     p.hr = (_Float16 *)(base + o_hr);
@@ -234,12 +235,19 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     if (err != hipSuccess)
         return cleanup(fail(MOE_E_HIP, "scratch initialisation failed: %s", hipGetErrorString(err)));
 
-    // Persistent grid per token count: resident blocks per CU x CUs.
-    const int kc = std::max(p.kc1, p.kc2);
+    // Per token count: the persistent grid (resident blocks per CU x CUs) and
+    // the 128-row blocks per gate/up item. With m >= 8 tokens (many row
+    // groups) a gate/up item covers two row blocks of one column split: one
+    // staging of the activations serves both, and there are about as many
+    // gate/up items as resident blocks. Fewer tokens keep one row block per
+    // item so that the few groups still spread over the grid.
+    const int kc = p.kc1;
     h->grid.assign(M + 1, 0);
     h->bpc.assign(M + 1, 0);
     h->lds.assign(M + 1, 0);
+    h->span1.assign(M + 1, 1);
     for (int m = 1; m <= (int)M; ++m) {
+        h->span1[m] = (m >= 8 && p.n_rb1 % 2 == 0) ? 2 : 1;
         const size_t lds = (size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) * sizeof(_Float16);
         int bpc = 0;
         err = expert_occupancy(p.format, p.kc1 / 128, &bpc, lds);
@@ -277,12 +285,14 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
     h->stream = s;
     Params p = h->p;
     p.out = out;
+    p.span1 = h->span1[m];
     HIP_TRY(launch_route(p, (const uint16_t *)x_bf16, logits, m, s));
     if (h->ev_begin)
         HIP_TRY(hipEventRecord(h->ev_begin, s));
     HIP_TRY(launch_expert(p, h->grid[m], h->lds[m], s));
     if (h->ev_end)
         HIP_TRY(hipEventRecord(h->ev_end, s));
+    HIP_TRY(launch_combine(p, m, s));
     h->ran = true;
     h->last_m = m;
     return MOE_OK;

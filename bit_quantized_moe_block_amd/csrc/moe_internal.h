@@ -19,7 +19,7 @@ constexpr int kLdsPadHalves = 8;    // 16 B row padding of the staged activation
 constexpr int kFmtCodebook = 1;
 constexpr int kFmtNvfp4 = 2;
 
-// Cross-block counters (rb_done, h_ready, comb) sit one per 128-byte line:
+// Cross-block counters (rb_done, h_ready) sit one per 128-byte line:
 // blocks polling one counter must not queue behind traffic to its
 // neighbours, as they would when packed.
 constexpr int kCtrStride = 32;  // uint32 per counter slot
@@ -63,7 +63,8 @@ struct Counters {
 struct Params {
     int32_t format, E, k, H, I, max_tokens;
     int32_t ks1, kc1;      // gate/up: column splits and columns per split
-    int32_t ks2, kc2;      // down: column splits and columns per split
+    int32_t ks2, kc2;      // down: column splits and columns per split (kc1 = kc2)
+    int32_t span1;         // gate/up: 128-row blocks per work item (set per run)
     int32_t n_rb1;         // I / 128 gate/up row blocks of 128 (one rotation block each)
     int32_t n_rb2;         // H / 256 down row blocks of 256
     int32_t pair_cap;      // max_tokens * k
@@ -86,14 +87,14 @@ struct Params {
     Counters *ctr;
     uint32_t *rb_done;     // [kMaxGroups][n_rb1] finished column splits per row block
     uint32_t *h_ready;     // [kMaxGroups] finished row blocks of h per row group
-    uint32_t *comb;        // [max_tokens][n_rb2] finished down contributions per token block
-                           // (all three: one counter per kCtrStride uint32)
+                           // (both: one counter per kCtrStride uint32)
 };
 
 // Kernel launchers (kernels.hip).
 hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits, int m,
                         hipStream_t s);
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s);
+hipError_t launch_combine(const Params &p, int m, hipStream_t s);
 // Occupancy of the expert kernel for a given dynamic LDS size.
 hipError_t expert_occupancy(int format, int ng, int *blocks_per_cu, size_t lds_bytes);
 
