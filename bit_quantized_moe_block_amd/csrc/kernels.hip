@@ -1,13 +1,13 @@
 // gfx950 kernels of the routed-experts decode step.
 //
-// route_kernel   1024-thread blocks. Block 0: top-k on the raw logits (one
-//                wave per token, DPP max-reductions), softmax over the
-//                selected logits, per-expert row buckets, row groups (<= 16
-//                rows each), the work plan, and a reset of the expert
-//                kernel's counters (so every run and every graph replay
-//                starts clean without a memset). Blocks 1..: one wave per
-//                (token, 128-column block) rotates x (codebook) or converts
-//                it to fp16 (NVFP4). No block waits on another.
+// route_kernel   256-thread blocks. The first blocks: top-k on the raw
+//                logits (one wave per token, DPP max-reductions), softmax
+//                over the selected logits; the last of them to finish builds
+//                the per-expert row buckets, row groups (<= 16 rows each), the
+//                work plan, and resets the expert kernel's counters (so every
+//                run and every graph replay starts clean without a memset).
+//                The other blocks: one wave per (token, 128-column block)
+//                rotates x (codebook) or converts it to fp16 (NVFP4).
 // expert_kernel  persistent grid, work items assigned round robin (no shared
 //                ticket counter), no grid-wide barrier. Gate/up items (one row group, 128 rows of gate and
 //                of up, one column split) write partial sums; the last split
@@ -115,7 +115,7 @@ __device__ __forceinline__ void wave_fwht128(float &v0, float &v1)
 // Route
 // ---------------------------------------------------------------------------
 
-constexpr int kRouteThreads = 1024;
+constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
 // Monotone key of a finite float: larger value <-> larger unsigned key; -0
@@ -151,7 +151,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int &total)
     int x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off);
+        const int y = __shfl_up(x, off);
         if (lane >= off)
             x += y;
     }
@@ -160,6 +160,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int &total)
     __syncthreads();
     int base = 0;
     total = 0;
+#pragma unroll
     for (int w = 0; w < kRouteWaves; ++w) {
         base += w < wave ? tmp[w] : 0;
         total += tmp[w];
@@ -168,56 +169,67 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int &total)
     return base + x - v;
 }
 
-__device__ void route_block(const Params &p, const float *__restrict__ logits, int m)
+__device__ __forceinline__ int ld_coherent_i32(const int32_t *p)
 {
-    __shared__ int s_ids[kMaxPairs];
-    __shared__ float s_val[kMaxPairs];
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Top-k of token t by one wave; lane holds experts lane + 64 i. Each round
+// takes the largest key, then the lowest expert id among equal keys; lane j
+// keeps slot j. Weights: softmax over the k selected logits, the denominator
+// summed in slot order. ids go out agent-coherent for the bucketing block.
+__device__ void route_token(const Params &p, const float *__restrict__ logits, int t)
+{
+    const int lane = threadIdx.x & 63;
+    const int E = p.E, k = p.k;
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? float_key(logits[(size_t)t * E + e]) : 0u;
+    }
+    int my_id = 0;
+    uint32_t my_key = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t kmax = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+        uint32_t cand = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 3; i >= 0; --i)
+            if (key[i] == kmax)
+                cand = lane + 64 * i;
+        const int e = (int)~wave_max_u32(~cand);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (e == lane + 64 * i)
+                key[i] = 0u;
+        if (lane == j) {
+            my_id = e;
+            my_key = kmax;
+        }
+    }
+    const float l0 = key_float(__builtin_amdgcn_readlane(my_key, 0));
+    const float ex = lane < k ? expf(key_float(my_key) - l0) : 0.0f;
+    float den = 0.0f;
+    for (int j = 0; j < k; ++j)
+        den += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+    if (lane < k) {
+        st_coherent((uint32_t *)&p.ids[t * k + lane], (uint32_t)my_id);
+        p.wts[t * k + lane] = ex / den;
+    }
+}
+
+// The last top-k block to finish builds the buckets: per-expert rows, row
+// groups (<= 16 rows each), the work plan, and clears the expert kernel's
+// counters (every run and every graph replay starts clean without a memset).
+__device__ void bucket_block(const Params &p, int m)
+{
     __shared__ uint32_t s_mask[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
     __shared__ int tmp[kRouteWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int E = p.E, k = p.k;
-    if (tid < kMaxExperts)
-        s_mask[tid] = 0u;
-
-    // ---- top-k: one wave per token; lane holds experts lane + 64 i. Each
-    // round takes the largest key, then the lowest expert id among equal keys.
-    for (int t = wave; t < m; t += kRouteWaves) {
-        uint32_t key[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            key[i] = e < E ? float_key(logits[(size_t)t * E + e]) : 0u;
-        }
-        for (int j = 0; j < k; ++j) {
-            const uint32_t kmax = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-            uint32_t cand = 0xFFFFFFFFu;
-#pragma unroll
-            for (int i = 3; i >= 0; --i)
-                if (key[i] == kmax)
-                    cand = lane + 64 * i;
-            const int e = (int)~wave_max_u32(~cand);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (e == lane + 64 * i)
-                    key[i] = 0u;
-            if (lane == 0) {
-                s_ids[t * k + j] = e;
-                s_val[t * k + j] = key_float(kmax);
-            }
-        }
-        // weights: softmax over the k selected logits, summed in slot order
-        if (lane == 0) {
-            const float l0 = s_val[t * k];
-            float den = 0.0f;
-            for (int j = 0; j < k; ++j)
-                den += expf(s_val[t * k + j] - l0);
-            for (int j = 0; j < k; ++j) {
-                p.ids[t * k + j] = s_ids[t * k + j];
-                p.wts[t * k + j] = expf(s_val[t * k + j] - l0) / den;
-            }
-        }
-    }
+    for (int e = tid; e < kMaxExperts; e += kRouteThreads)
+        s_mask[e] = 0u;
     __syncthreads();
 
     // ---- buckets. Top-k picks distinct experts per token, so expert e's rows
@@ -225,7 +237,7 @@ __device__ void route_block(const Params &p, const float *__restrict__ logits, i
     // the rank of (t, j) inside e's bucket is popcount(mask[e] below bit t).
     const int np = m * k;
     for (int i = tid; i < np; i += kRouteThreads)
-        atomicOr(&s_mask[s_ids[i]], 1u << (i / k));
+        atomicOr(&s_mask[ld_coherent_i32(&p.ids[i])], 1u << (i / k));
     __syncthreads();
     const uint32_t mask = tid < E ? s_mask[tid] : 0u;
     const int cnt = __popc(mask);
@@ -249,7 +261,7 @@ __device__ void route_block(const Params &p, const float *__restrict__ logits, i
     }
     __syncthreads();
     for (int i = tid; i < np; i += kRouteThreads) {
-        const int e = s_ids[i], t = i / k;
+        const int e = ld_coherent_i32(&p.ids[i]), t = i / k;
         const int q = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
         p.rows[q] = i;
         p.pos[i] = q;
@@ -272,18 +284,37 @@ __device__ void route_block(const Params &p, const float *__restrict__ logits, i
         p.h_ready[i * kCtrStride] = 0;
 }
 
+// Blocks 0 .. ceil(m / kRouteWaves) - 1: one wave per token does its top-k;
+// the last of these blocks to finish (one counter) buckets the rows. The
+// remaining blocks: one wave per (token, 128-column block) rotates x
+// (codebook) or converts it to fp16 (NVFP4).
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
                                                               const uint16_t *__restrict__ x,
                                                               const float *__restrict__ logits,
                                                               int m)
 {
-    if (blockIdx.x == 0) {
-        route_block(p, logits, m);
+    __shared__ int s_last;
+    const int nk = (m + kRouteWaves - 1) / kRouteWaves;
+    const int wave = threadIdx.x >> 6;
+    if ((int)blockIdx.x < nk) {
+        const int t = blockIdx.x * kRouteWaves + wave;
+        if (t < m)
+            route_token(p, logits, t);
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            s_last = atomic_add_agent(&p.ctr->route_done, 1u) == (uint32_t)(nk - 1);
+            if (s_last)  // every top-k block has counted: clear for the next run
+                __hip_atomic_store(&p.ctr->route_done, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (s_last)
+            bucket_block(p, m);
         return;
     }
-    // one wave per (token, 128-column block) of the activations
     const int lane = threadIdx.x & 63;
-    const int task = (blockIdx.x - 1) * kRouteWaves + (threadIdx.x >> 6);
+    const int task = (blockIdx.x - nk) * kRouteWaves + wave;
     const int nb = p.H / 128;
     if (task >= m * nb)
         return;
@@ -1011,8 +1042,8 @@ hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits,
                         hipStream_t s)
 {
     const int tasks = m * (p.H / 128);
-    route_kernel<<<dim3(1 + (tasks + kRouteWaves - 1) / kRouteWaves), dim3(kRouteThreads), 0, s>>>(
-        p, x, logits, m);
+    const int blocks = (m + kRouteWaves - 1) / kRouteWaves + (tasks + kRouteWaves - 1) / kRouteWaves;
+    route_kernel<<<dim3(blocks), dim3(kRouteThreads), 0, s>>>(p, x, logits, m);
     return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ constexpr int kDoneSlots = 8;
 struct Counters {
     uint32_t items_done[kDoneSlots];  // work items completed (statistics)
     uint32_t error_word;              // kErr* bits
-    uint32_t pad[7];
+    uint32_t route_done;              // top-k blocks finished (route kernel)
+    uint32_t pad[6];
 };
 
 // Everything a kernel needs, passed by value.
