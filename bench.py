@@ -231,12 +231,13 @@ def main():
 
     # ---- dominant kernel alone: HIP events recorded by the library right
     # before and after the expert kernel, on the stream it is launched on.
+    # Each pass launches every layer back to back (the host enqueues far
+    # faster than the layers run) and reads the events after one
+    # synchronisation. (Events recorded by graph nodes cannot be timed.)
     import bit_quantized_moe_block_amd as B
     evs = [(HipEvent(), HipEvent()) for _ in layers]
     for layer, (eb, ee) in zip(layers, evs):
         B.moe_decode_profile_events(layer.handle, eb.ptr, ee.ptr)
-    # each pass launches every layer back to back (as the graph does) and
-    # reads the events after one synchronisation
     kern_ms, kern_bytes = [], []
     with torch.cuda.stream(stream):
         for _ in range(args.profile_passes):
