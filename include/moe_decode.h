@@ -63,10 +63,13 @@ typedef enum { MOE_FMT_CODEBOOK = 1, MOE_FMT_NVFP4 = 2 } moe_format;
  * MOE_FMT_CODEBOOK (bits = 2 or 3): stand-in for the 2/3-bit codes that the
  * pages name but do not define (page "lna-lab/README.md", "What is in the
  * pack"). Weights live in the rotated basis (see signs_* below).
- *   codes  : uint32 words, bits words per slot (tile = 64*bits words). Column
- *            jj of a slot (d = jj/16, kk = jj%16): low two code bits at word d,
- *            bit 8(kk%4) + 2(kk/4); for bits = 3 the high bit at word 2,
- *            bit 8(kk%4) + kk/4 + 4d. 4-byte aligned.
+ *   codes  : uint32 words, bits words per slot (tile = 64*bits words),
+ *            4-byte aligned. Column jj of a slot, code bits LSB first:
+ *            bits = 2 (d = jj/16, kk = jj%16): word d, bits 8(kk%4) + 2(kk/4)
+ *            and +1. bits = 3, jj < 24 (d = jj/8, i = jj%8): word d, bits
+ *            8(i%4) + 3(i/4) + 0..2; jj >= 24 (i = jj-24): bits 0 and 1 at
+ *            word i/4, bits 8(i%4) + 6 and + 7, bit 2 at word 2, bit
+ *            8(i%4) + 6 + i/4.
  *   scales : fp16, one per (row, 128-column group), row-major:
  *            scales[n*(C/128) + c/128]. 16-byte aligned.
  *   lut    : fp16[2^bits] codebook. W[n][c] = lut[code] * scale.

@@ -158,9 +158,41 @@ void orc_unrotate(int n, const int8_t *signs, const double *in, double *out)
  */
 
 /* Codebook, K = bits in {2,3}: each slot is K little-endian uint32 words
- * w0..w(K-1). Column jj of the slot, with d = jj div 16 and kk = jj mod 16:
- *   low two code bits at w_d, bits 8 (kk mod 4) + 2 (kk div 4) and +1;
- *   K = 3: the high code bit at w_2, bit 8 (kk mod 4) + (kk div 4) + 4 d. */
+ * w0..w(K-1). Column jj (0..31) of the slot takes its code bits, least
+ * significant first, from these (word, bit) positions:
+ *   K = 3, jj < 24:  d = jj div 8, i = jj mod 8: word d, bits
+ *                    8 (i mod 4) + 3 (i div 4) + {0, 1, 2};
+ *   K = 3, 24..31:   i = jj - 24: bits 0 and 1 at word i div 4, bits
+ *                    8 (i mod 4) + 6 + {0, 1}; bit 2 at word 2, bit 8 (i mod 4) + 6 + i div 4;
+ *   K = 2:           d = jj div 16, kk = jj mod 16: word d, bits
+ *                    8 (kk mod 4) + 2 (kk div 4) + {0, 1}.
+ * Every bit of the K words holds exactly one code bit. */
+static void codebook_bit_positions(int bits, int jj, int word[3], int bit[3])
+{
+    int k;
+    if (bits == 3 && jj < 24) {
+        int i = jj % 8;
+        for (k = 0; k < 3; ++k) {
+            word[k] = jj / 8;
+            bit[k] = 8 * (i % 4) + 3 * (i / 4) + k;
+        }
+    } else if (bits == 3) {
+        int i = jj - 24;
+        for (k = 0; k < 2; ++k) {
+            word[k] = i / 4;
+            bit[k] = 8 * (i % 4) + 6 + k;
+        }
+        word[2] = 2;
+        bit[2] = 8 * (i % 4) + 6 + i / 4;
+    } else {
+        int kk = jj % 16;
+        for (k = 0; k < 2; ++k) {
+            word[k] = jj / 16;
+            bit[k] = 8 * (kk % 4) + 2 * (kk / 4) + k;
+        }
+    }
+}
+
 uint32_t orc_codebook_code(int bits, int N, int C, const uint32_t *codes, int n, int c)
 {
     (void)N;
@@ -170,10 +202,11 @@ uint32_t orc_codebook_code(int bits, int N, int C, const uint32_t *codes, int n,
     int slot = q * 16 + r;
     long tau = (long)rb * G + g;
     const uint32_t *w = codes + (tau * 64 + slot) * bits;
-    int d = jj / 16, kk = jj % 16;
-    uint32_t code = (w[d] >> (8 * (kk % 4) + 2 * (kk / 4))) & 3u;
-    if (bits == 3)
-        code |= ((w[2] >> (8 * (kk % 4) + (kk / 4) + 4 * d)) & 1u) << 2;
+    int word[3], bit[3], k;
+    uint32_t code = 0;
+    codebook_bit_positions(bits, jj, word, bit);
+    for (k = 0; k < bits; ++k)
+        code |= ((w[word[k]] >> bit[k]) & 1u) << k;
     return code;
 }
 

@@ -46,16 +46,36 @@ def bf16_to_f64(bits):
 
 # ----------------------------------------------------------- layouts
 
+def _byte_contents(bits):
+    """What each byte of a slot holds, byte by byte: for word d and byte b,
+    a list of (bit-in-byte, column, code bit). The opposite view from the
+    oracle's column-by-column positions."""
+    out = {}
+    for b in range(4):
+        if bits == 3:
+            for d in range(3):
+                # two whole 3-bit codes: columns 8d + b and 8d + 4 + b
+                out[d, b] = ([(k, 8 * d + b, k) for k in range(3)]
+                             + [(3 + k, 8 * d + 4 + b, k) for k in range(3)])
+            # bits 6-7: the two low bits of column 24 + b (word 0) / 28 + b
+            # (word 1); word 2 keeps their high bits
+            out[0, b] += [(6, 24 + b, 0), (7, 24 + b, 1)]
+            out[1, b] += [(6, 28 + b, 0), (7, 28 + b, 1)]
+            out[2, b] += [(6, 24 + b, 2), (7, 28 + b, 2)]
+        else:
+            for d in range(2):
+                out[d, b] = [(2 * sh + k, 16 * d + 4 * sh + b, k) for sh in range(4) for k in range(2)]
+    return out
+
+
 def _slot_bit_tables(bits):
     """For slot column jj (0..31): (word, bit) of each code bit, LSB first."""
-    tab = []
-    for jj in range(32):
-        d, kk = divmod(jj, 16)
-        lo = 8 * (kk % 4) + 2 * (kk // 4)
-        entry = [(d, lo), (d, lo + 1)]
-        if bits == 3:
-            entry.append((2, 8 * (kk % 4) + (kk // 4) + 4 * d))
-        tab.append(entry)
+    tab = [[None] * bits for _ in range(32)]
+    for (d, b), items in _byte_contents(bits).items():
+        for bit_in_byte, col, sig in items:
+            assert tab[col][sig] is None
+            tab[col][sig] = (d, 8 * b + bit_in_byte)
+    assert all(e is not None for entry in tab for e in entry)
     return tab
 
 

@@ -107,10 +107,11 @@ def test_codebook_layout_matches_unpackbits_decoder(bits, shape):
 
 def test_codebook_layout_hand_values():
     # Hand-derived from the layout definition (tiles of 16x128, slot l = row
-    # l mod 16 / columns 32 (l div 16).., low bits of column kk of word d at
-    # bit 8 (kk mod 4) + 2 (kk div 4)): a slot word 0xFFAA5500 holds code
-    # kk mod 4 for kk = 0..15, i.e. byte b repeats code b.
+    # l mod 16 / columns 32 (l div 16)..+31, K words per slot).
     N, C = 16, 128
+    # K = 2: low bits of column kk of word d at bit 8 (kk mod 4) + 2 (kk div 4):
+    # a slot word 0xFFAA5500 holds code kk mod 4 for kk = 0..15 (byte b
+    # repeats code b).
     words = np.zeros(N * C * 2 // 32, np.uint32)
     words[0] = 0xFFAA5500          # slot 0 (row 0, cols 0..15)
     words[1] = 0x000000FF          # slot 0, cols 16..31: code 3 at kk = 0,4,8,12
@@ -120,11 +121,34 @@ def test_codebook_layout_hand_values():
     assert got[16:] == [3 if kk % 4 == 0 else 0 for kk in range(16)]
     assert oracle.codebook_code(2, N, C, words, 1, 32) == 3
     assert oracle.codebook_code(2, N, C, words, 1, 33) == 0
-    # K = 3: high bit of column (d, kk) at word 2, bit 8 (kk mod 4) + kk div 4 + 4 d.
+    # K = 3: word d < 3, byte b: bits 0-2 = column 8d + b, bits 3-5 = column
+    # 8d + 4 + b; bits 6-7 of words 0 / 1 = low bits of columns 24 + b /
+    # 28 + b, whose high bits are bits 6 / 7 of byte b of word 2.
     w3 = np.zeros(N * C * 3 // 32, np.uint32)
-    w3[2] = 1 << (8 * 1 + 2 + 4)   # slot 0, d = 1, kk = 9 (kk mod 4 = 1, kk div 4 = 2)
-    assert oracle.codebook_code(3, N, C, w3, 0, 16 + 9) == 4
-    assert sum(oracle.codebook_code(3, N, C, w3, 0, c) for c in range(128)) == 4
+    w3[0] = 0x00003800             # byte 1 bits 3-5 -> column 5 = 7
+    w3[1] = 0x00000040             # byte 0 bit 6 -> column 28, bit 0
+    w3[2] = 0x80000007             # byte 0 bits 0-2 -> column 16 = 7; bit 31 -> column 31, bit 2
+    got = [oracle.codebook_code(3, N, C, w3, 0, c) for c in range(128)]
+    want = [0] * 128
+    want[5], want[16], want[28], want[31] = 7, 7, 1, 4
+    assert got == want
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_codebook_layout_is_a_bijection(bits):
+    # Every bit of a slot's K words belongs to exactly one code bit: setting
+    # one stored bit changes exactly one code, by exactly one power of two.
+    N, C = 16, 128
+    seen = set()
+    for d in range(bits):
+        for bit in range(32):
+            words = np.zeros(N * C * bits // 32, np.uint32)
+            words[d] = np.uint32(1 << bit)   # slot 0: row 0, columns 0..31
+            codes = [oracle.codebook_code(bits, N, C, words, 0, c) for c in range(32)]
+            nz = [(c, v) for c, v in enumerate(codes) if v]
+            assert len(nz) == 1 and bin(nz[0][1]).count("1") == 1, (d, bit, nz)
+            seen.add(nz[0])
+    assert len(seen) == 32 * bits
 
 
 @pytest.mark.parametrize("bits", [2, 3])
