@@ -62,9 +62,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack43",
-                    choices=["stack43", "full_layer", "rank_share", "nvfp4", "tiny"])
+                    choices=["stack43", "pack46", "full_layer", "rank_share", "nvfp4", "tiny"])
     ap.add_argument("--m", type=int, default=None, help="tokens per step (default: workload's)")
-    ap.add_argument("--layers", type=int, default=None, help="layers of the stack (default 43)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers of the stack (default: the workload's, 43 for stack43)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-passes", type=int, default=3)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -128,7 +129,7 @@ def main():
 
     w = WORKLOADS[args.workload]
     m = args.m or (16 if args.workload in ("stack43", "full_layer") else w.max_tokens)
-    n_layers = args.layers or (w.layers if args.workload == "stack43" else 1)
+    n_layers = args.layers or w.layers
     stacked = n_layers > 1
     dev = torch.device("cuda")
     torch.cuda.init()

@@ -21,7 +21,7 @@ class Workload:
     hidden: int
     inter: int
     fmt: str                # "codebook" or "nvfp4"
-    bits_mix: str           # "all2" | "alternate" | "mix62" | "nvfp4"
+    bits_mix: str           # "all2" | "alternate" | "mix62" | "pack" | "nvfp4"
     router: str             # "normal" | "zipf"
     token_counts: Tuple[int, ...]
     layers: int = 1
@@ -30,6 +30,11 @@ class Workload:
     @property
     def max_tokens(self) -> int:
         return max(self.token_counts)
+
+
+# Layers of the "pack" mix whose routed experts are all 2-bit: the three
+# replaced routed layers and the three MTP draft layers after the 43 routed ones.
+PACK_ALL2_LAYERS = (3, 21, 41, 43, 44, 45)
 
 
 WORKLOADS = {
@@ -44,6 +49,11 @@ WORKLOADS = {
     # 43 such layers back to back at the 16-row decode batch.
     "stack43": Workload("stack43", 4, 256, 8, 4096, 2048, "codebook", "mix62", "zipf",
                         (16,), layers=43),
+    # The pack as shipped (lna-lab README, "What is in the pack"): the 43 routed
+    # layers with layers 3, 21 and 41 all 2-bit, followed by the 3 MTP draft
+    # MoE layers, all 2-bit (layers 43..45), same shapes, 16 rows per step.
+    "pack46": Workload("pack46", 6, 256, 8, 4096, 2048, "codebook", "pack", "zipf",
+                       (16,), layers=46),
     # NVFP4 experts (e2m1 values, e4m3 per-16 scales, fp32 tensor scale).
     "nvfp4": Workload("nvfp4", 5, 256, 8, 4096, 2048, "nvfp4", "nvfp4", "normal", (2, 8)),
 }

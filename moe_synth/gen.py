@@ -26,7 +26,7 @@ import os
 
 import numpy as np
 
-from .configs import Workload
+from .configs import PACK_ALL2_LAYERS, Workload
 
 TAG_X, TAG_LOGITS, TAG_SIGN_H, TAG_SIGN_I, TAG_ZIPF, TAG_KMIX, TAG_CODES, TAG_LUT, \
     TAG_SCALES, TAG_TSCALE = range(10)
@@ -63,12 +63,14 @@ def expert_bits(w: Workload, layer: int = 0) -> np.ndarray:
         return np.full(E, 3, np.int32)
     if w.bits_mix == "alternate":
         return (2 + (np.arange(E) % 2)).astype(np.int32)
-    if w.bits_mix == "mix62":
+    if w.bits_mix == "mix62" or (w.bits_mix == "pack" and layer not in PACK_ALL2_LAYERS):
         n3 = (E * 5) // 8
         pick = _rng(w.config_id, layer, TAG_KMIX).permutation(E)[:n3]
         b = np.full(E, 2, np.int32)
         b[pick] = 3
         return b
+    if w.bits_mix == "pack":
+        return np.full(E, 2, np.int32)
     if w.bits_mix == "nvfp4":
         return np.full(E, 4, np.int32)
     raise ValueError(w.bits_mix)

@@ -98,6 +98,29 @@ def test_full_layer_sampled(full_layer, m):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("layer", [3, 20, 43])
+def test_pack_layers_sampled(layer):
+    # The pack mix at full size and the 16-row batch: an all-2-bit routed layer,
+    # a mixed layer and an MTP draft layer, sampled tokens against the oracle.
+    w = WORKLOADS["pack46"]
+    m = 16
+    case = gen.make_case(w, m, layer=layer)
+    tokens = [0, 7, 15]
+    say(f"[parity] pack46 layer={layer} m={m}")
+    dl = DeviceLayer.from_case(case, max_tokens=m)
+    try:
+        out = run_gpu(dl, case)
+        check_routing(dl, case, m)
+        st = dl.stats()
+        assert st.error_word == 0 and st.items_done == st.items
+        ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+        err = rel_err(out, ref["out"], tokens)
+        say(f"    rel={err:.3e} hit={st.hit_experts}")
+        assert err <= REL_TOL
+    finally:
+        dl.close()
+
+
 def test_bitwise_repeatable_and_graph_replay():
     w = small_workload("rep", 16, 4, 1024, 256, bits_mix="alternate", config_id=301)
     case = gen.make_case(w, 24)

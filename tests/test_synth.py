@@ -46,6 +46,20 @@ def test_mixed_bits_is_five_eighths_three_bit():
     assert avg == 2.75
 
 
+def test_pack_mix_layers():
+    # The pack: 43 routed layers with 3, 21 and 41 all 2-bit, then 3 MTP draft
+    # layers, all 2-bit; every other layer has the 5/8 three-bit mix.
+    w = WORKLOADS["pack46"]
+    assert w.layers == 46 and w.max_tokens == 16
+    all2 = [l for l in range(w.layers) if (gen.expert_bits(w, l) == 2).all()]
+    assert all2 == [3, 21, 41, 43, 44, 45]
+    for l in (0, 20, 42):
+        b = gen.expert_bits(w, l)
+        assert (b == 3).sum() == 160 and (b == 2).sum() == 96
+    # the mixed layers are drawn per layer, not repeated
+    assert not np.array_equal(gen.expert_bits(w, 0), gen.expert_bits(w, 1))
+
+
 def test_bf16_rounding_matches_torch():
     a = np.random.default_rng(0).standard_normal(10000).astype(np.float32)
     ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
