@@ -26,6 +26,7 @@ class Workload:
     token_counts: Tuple[int, ...]
     layers: int = 1
     zipf_s: float = 1.1
+    shared_bits: int = 0    # > 0: an always-on shared expert with these codebook bits
 
     @property
     def max_tokens(self) -> int:
@@ -54,13 +55,22 @@ WORKLOADS = {
     # MoE layers, all 2-bit (layers 43..45), same shapes, 16 rows per step.
     "pack46": Workload("pack46", 6, 256, 8, 4096, 2048, "codebook", "pack", "zipf",
                        (16,), layers=46),
+    # The full layer plus its always-on shared expert, stored 6-bit like the
+    # pack's dense linears (lna-lab README, "What is in the pack": attention
+    # and shared experts in EXL3 6 bit); the shared expert has the routed
+    # experts' shape.
+    "shared_layer": Workload("shared_layer", 7, 256, 8, 4096, 2048, "codebook", "mix62", "zipf",
+                             (1, 16, 24), shared_bits=6),
+    # The 43-layer stack with the shared expert in every layer.
+    "stack43_shared": Workload("stack43_shared", 8, 256, 8, 4096, 2048, "codebook", "mix62",
+                               "zipf", (16,), layers=43, shared_bits=6),
     # NVFP4 experts (e2m1 values, e4m3 per-16 scales, fp32 tensor scale).
     "nvfp4": Workload("nvfp4", 5, 256, 8, 4096, 2048, "nvfp4", "nvfp4", "normal", (2, 8)),
 }
 
 
 def small_workload(name, num_experts, top_k, hidden, inter, fmt="codebook",
-                   bits_mix="alternate", router="normal", config_id=100):
+                   bits_mix="alternate", router="normal", config_id=100, shared_bits=0):
     """A reduced shape for fast tests (same recipe, smaller sizes)."""
     return Workload(name, config_id, num_experts, top_k, hidden, inter, fmt, bits_mix,
-                    router, (1,))
+                    router, (1,), shared_bits=shared_bits)

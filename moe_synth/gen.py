@@ -139,7 +139,8 @@ def make_tensor(w: Workload, layer: int, e: int, proj: int, bits: int) -> dict:
 def make_layer(w: Workload, layer: int = 0, experts=None, threads=None) -> dict:
     """All stored tensors of one layer (or of the given experts only).
 
-    Returns dict(bits [E], tensors {(e, proj): tensor}, signs_hidden, signs_inter).
+    Returns dict(bits [E], tensors {(e, proj): tensor}, shared ({proj: tensor}
+    or None), shared_bits, signs_hidden, signs_inter).
     """
     bits = expert_bits(w, layer)
     ex = range(w.num_experts) if experts is None else sorted(set(int(e) for e in experts))
@@ -148,7 +149,12 @@ def make_layer(w: Workload, layer: int = 0, experts=None, threads=None) -> dict:
     with _cf.ThreadPoolExecutor(threads) as pool:
         out = list(pool.map(lambda ep: make_tensor(w, layer, ep[0], ep[1], int(bits[ep[0]])), jobs))
     tensors = {ep: t for ep, t in zip(jobs, out)}
-    d = dict(bits=bits, tensors=tensors)
+    d = dict(bits=bits, tensors=tensors, shared=None, shared_bits=0)
+    if w.shared_bits:
+        # the shared expert draws as expert index E (its own seed namespace)
+        d["shared"] = {p: make_tensor(w, layer, w.num_experts, p, w.shared_bits)
+                       for p in (PROJ_GATE, PROJ_UP, PROJ_DOWN)}
+        d["shared_bits"] = w.shared_bits
     if w.fmt == "codebook":
         d["signs_hidden"] = make_signs(w, layer, "hidden")
         d["signs_inter"] = make_signs(w, layer, "inter")

@@ -81,7 +81,7 @@ class _Layer(C.Structure):
                 ("hidden", C.c_int32), ("inter", C.c_int32), ("bits", C.c_void_p),
                 ("codes", C.c_void_p), ("scales", C.c_void_p), ("luts", C.c_void_p),
                 ("tscales", C.c_void_p), ("signs_hidden", C.c_void_p),
-                ("signs_inter", C.c_void_p)]
+                ("signs_inter", C.c_void_p), ("has_shared", C.c_int32)]
 
 
 class Layer:
@@ -89,18 +89,25 @@ class Layer:
 
     fmt: "codebook" or "nvfp4"; tensors: {(e, proj): dict(codes, scales, lut,
     tensor_scale)}; experts missing from `tensors` must never be routed to.
+    shared: None, or {proj: tensor} of the shared expert (codebook format,
+    `shared_bits` bits), stored as expert E.
     """
 
     def __init__(self, fmt, num_experts, top_k, hidden, inter, bits, tensors,
-                 signs_hidden=None, signs_inter=None):
+                 signs_hidden=None, signs_inter=None, shared=None, shared_bits=0):
         E = num_experts
         self.keep = []
-        self.bits = np.ascontiguousarray(bits, dtype=np.int32)
-        codes = (C.c_void_p * (3 * E))()
-        scales = (C.c_void_p * (3 * E))()
-        luts = (C.c_void_p * (3 * E))()
-        ts = np.zeros(3 * E, np.float32)
-        for (e, p), t in tensors.items():
+        self.bits = np.zeros(E + 1, np.int32)
+        self.bits[:E] = np.asarray(bits, dtype=np.int32)
+        self.bits[E] = shared_bits if shared else 0
+        codes = (C.c_void_p * (3 * E + 3))()
+        scales = (C.c_void_p * (3 * E + 3))()
+        luts = (C.c_void_p * (3 * E + 3))()
+        ts = np.zeros(3 * E + 3, np.float32)
+        items = list(tensors.items())
+        if shared:
+            items += [((E, p), t) for p, t in shared.items()]
+        for (e, p), t in items:
             c = np.ascontiguousarray(t["codes"])
             s = np.ascontiguousarray(t["scales"])
             self.keep += [c, s]
@@ -118,14 +125,15 @@ class Layer:
                         self.bits.ctypes.data, C.cast(codes, C.c_void_p),
                         C.cast(scales, C.c_void_p), C.cast(luts, C.c_void_p), ts.ctypes.data,
                         None if self.sh is None else self.sh.ctypes.data,
-                        None if self.si is None else self.si.ctypes.data)
+                        None if self.si is None else self.si.ctypes.data, 1 if shared else 0)
         self.fmt, self.E, self.k, self.H, self.I = fmt, E, top_k, hidden, inter
 
     @classmethod
     def from_case(cls, case):
         w = case["workload"]
         return cls(w.fmt, w.num_experts, w.top_k, w.hidden, w.inter, case["bits"],
-                   case["tensors"], case["signs_hidden"], case["signs_inter"])
+                   case["tensors"], case["signs_hidden"], case["signs_inter"],
+                   case.get("shared"), case.get("shared_bits", 0))
 
     def ptr(self):
         return C.cast(C.pointer(self.s), C.c_void_p)

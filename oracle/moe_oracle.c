@@ -157,7 +157,7 @@ void orc_unrotate(int n, const int8_t *signs, const double *in, double *out)
  * 128g + 32 (l div 16) + jj, jj = 0..31; slots are stored in order.
  */
 
-/* Codebook, K = bits in {2,3}: each slot is K little-endian uint32 words
+/* Codebook, K = bits in {2,3,6}: each slot is K little-endian uint32 words
  * w0..w(K-1). Column jj (0..31) of the slot takes its code bits, least
  * significant first, from these (word, bit) positions:
  *   K = 3, jj < 24:  d = jj div 8, i = jj mod 8: word d, bits
@@ -165,11 +165,21 @@ void orc_unrotate(int n, const int8_t *signs, const double *in, double *out)
  *   K = 3, 24..31:   i = jj - 24: bits 0 and 1 at word i div 4, bits
  *                    8 (i mod 4) + 6 + {0, 1}; bit 2 at word 2, bit 8 (i mod 4) + 6 + i div 4;
  *   K = 2:           d = jj div 16, kk = jj mod 16: word d, bits
- *                    8 (kk mod 4) + 2 (kk div 4) + {0, 1}.
+ *                    8 (kk mod 4) + 2 (kk div 4) + {0, 1};
+ *   K = 6:           the slot read as one 192-bit little-endian string:
+ *                    bits 6 jj .. 6 jj + 5 (word q div 32, bit q mod 32 for
+ *                    string bit q).
  * Every bit of the K words holds exactly one code bit. */
-static void codebook_bit_positions(int bits, int jj, int word[3], int bit[3])
+static void codebook_bit_positions(int bits, int jj, int word[6], int bit[6])
 {
     int k;
+    if (bits == 6) {
+        for (k = 0; k < 6; ++k) {
+            word[k] = (6 * jj + k) / 32;
+            bit[k] = (6 * jj + k) % 32;
+        }
+        return;
+    }
     if (bits == 3 && jj < 24) {
         int i = jj % 8;
         for (k = 0; k < 3; ++k) {
@@ -202,7 +212,7 @@ uint32_t orc_codebook_code(int bits, int N, int C, const uint32_t *codes, int n,
     int slot = q * 16 + r;
     long tau = (long)rb * G + g;
     const uint32_t *w = codes + (tau * 64 + slot) * bits;
-    int word[3], bit[3], k;
+    int word[6], bit[6], k;
     uint32_t code = 0;
     codebook_bit_positions(bits, jj, word, bit);
     for (k = 0; k < bits; ++k)
@@ -317,6 +327,8 @@ typedef struct {
     const float *tscales;     /* [E*3] tensor scales (NVFP4) */
     const int8_t *signs_hidden; /* [hidden] (codebook) */
     const int8_t *signs_inter;  /* [inter] (codebook) */
+    int32_t has_shared;         /* 1: expert E is a shared expert (codebook format):
+                                 * bits[E], tensors 3E..3E+2, same H and I */
 } orc_layer;
 
 static double weight_at(const orc_layer *L, int e, int p, int N, int C, int n, int c)
@@ -371,6 +383,10 @@ void orc_expert(const orc_layer *L, int e, const double *xr, double *y)
  * tokens whose expert FFNs are evaluated; routing and buckets always cover
  * all m tokens. out [m*H] (rows of unselected tokens are left untouched),
  * ids [m*k], w [m*k], y_pairs [m*k*H] (optional: per (t, j) expert output).
+ * With a shared expert (has_shared), every selected token also runs expert
+ * E, and its output is added with weight 1 after the k routed terms: the
+ * always-on shared expert of the DeepSeek MoE block ("lna-lab/README.md",
+ * "What is in the pack": shared experts among the dense linears).
  * Returns the number of OpenMP threads used. */
 int orc_moe_layer(const orc_layer *L, int m, const uint16_t *x_bf16, const float *logits,
                   const uint8_t *token_mask, double *out, int32_t *ids, double *w,
@@ -404,6 +420,9 @@ int orc_moe_layer(const orc_layer *L, int m, const uint16_t *x_bf16, const float
     }
 
     double *ys = (double *)malloc(sizeof(double) * (size_t)(npairs ? npairs : 1) * H);
+    double *ysh = NULL;  /* shared expert output per token */
+    if (L->has_shared)
+        ysh = (double *)malloc(sizeof(double) * (size_t)(m ? m : 1) * H);
     int used = 1;
 #pragma omp parallel
     {
@@ -412,9 +431,14 @@ int orc_moe_layer(const orc_layer *L, int m, const uint16_t *x_bf16, const float
         used = omp_get_num_threads();
 #endif
 #pragma omp for schedule(dynamic, 1)
-        for (int p = 0; p < npairs; ++p) {
-            int t = pair_t[p], j = pair_j[p];
-            orc_expert(L, ids[t * k + j], xr + (size_t)t * H, ys + (size_t)p * H);
+        for (int p = 0; p < npairs + (L->has_shared ? npairs / (k ? k : 1) : 0); ++p) {
+            if (p < npairs) {
+                int t = pair_t[p], j = pair_j[p];
+                orc_expert(L, ids[t * k + j], xr + (size_t)t * H, ys + (size_t)p * H);
+            } else {
+                int t = pair_t[(p - npairs) * k];
+                orc_expert(L, E, xr + (size_t)t * H, ysh + (size_t)t * H);
+            }
         }
     }
 
@@ -425,6 +449,8 @@ int orc_moe_layer(const orc_layer *L, int m, const uint16_t *x_bf16, const float
             double acc = 0.0;
             for (int j = 0; j < k; ++j)
                 acc += w[t * k + j] * ys[(size_t)(p0 + j) * H + i];
+            if (ysh)
+                acc += ysh[(size_t)t * H + i];
             out[(size_t)t * H + i] = acc;
         }
         if (y_pairs)
@@ -433,6 +459,7 @@ int orc_moe_layer(const orc_layer *L, int m, const uint16_t *x_bf16, const float
                        sizeof(double) * H);
     }
     free(ys);
+    free(ysh);
     free(xr);
     free(pair_t);
     free(pair_j);

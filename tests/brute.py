@@ -51,6 +51,12 @@ def _byte_contents(bits):
     a list of (bit-in-byte, column, code bit). The opposite view from the
     oracle's column-by-column positions."""
     out = {}
+    if bits == 6:
+        # the slot as a 192-bit string: string bit q is bit q mod 8 of byte q div 8
+        # (word q div 32, byte (q div 8) mod 4), and code bit q mod 6 of column q div 6
+        for q in range(192):
+            out.setdefault((q // 32, (q // 8) % 4), []).append((q % 8, q // 6, q % 6))
+        return out
     for b in range(4):
         if bits == 3:
             for d in range(3):
@@ -188,4 +194,20 @@ def layer_plain(case, ids=None, w=None):
             Wg, Wu, Wd = cache[e]
             y = Wd @ (silu(Wg @ x[t]) * (Wu @ x[t]))
             out[t] += w[t, j] * y
+    if case.get("shared"):
+        out += shared_plain(case)
     return out
+
+
+def shared_plain(case):
+    """The shared expert's FFN of every token, plain basis, dense fp64."""
+    wl = case["workload"]
+    H, I = wl.hidden, wl.inter
+    x = bf16_to_f64(case["x"])
+    RH = rotation_matrix(case["signs_hidden"])
+    RI = rotation_matrix(case["signs_inter"])
+    sh = case["shared"]
+    Wg = dense(wl.fmt, sh[0], I, H) @ RH
+    Wu = dense(wl.fmt, sh[1], I, H) @ RH
+    Wd = dense(wl.fmt, sh[2], H, I) @ RI
+    return np.stack([Wd @ (silu(Wg @ x[t]) * (Wu @ x[t])) for t in range(x.shape[0])])

@@ -93,7 +93,7 @@ def test_rotation_dense_and_roundtrip(n):
 
 # ------------------------------------------------------------ stored layouts
 
-@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("bits", [2, 3, 6])
 @pytest.mark.parametrize("shape", [(16, 128), (32, 256), (48, 384)])
 def test_codebook_layout_matches_unpackbits_decoder(bits, shape):
     N, C = shape
@@ -132,9 +132,20 @@ def test_codebook_layout_hand_values():
     want = [0] * 128
     want[5], want[16], want[28], want[31] = 7, 7, 1, 4
     assert got == want
+    # K = 6: column jj at bits 6 jj .. 6 jj + 5 of the slot's 192-bit string.
+    # Column 0 = bits 0-5 of word 0; column 5 straddles words 0 and 1 (bits 30,
+    # 31 of word 0 are its code bits 0, 1); column 31 = bits 26-31 of word 5.
+    w6 = np.zeros(N * C * 6 // 32, np.uint32)
+    w6[0] = 0x8000002A             # column 0 = 0b101010 = 42; word 0 bit 31 -> column 5 bit 1
+    w6[1] = 0x00000005             # word 1 bits 0, 2 -> column 5 bits 2, 4
+    w6[5] = 0xFC000000             # column 31 = 63
+    got = [oracle.codebook_code(6, N, C, w6, 0, c) for c in range(128)]
+    want = [0] * 128
+    want[0], want[5], want[31] = 42, 2 + 4 + 16, 63
+    assert got == want
 
 
-@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("bits", [2, 3, 6])
 def test_codebook_layout_is_a_bijection(bits):
     # Every bit of a slot's K words belongs to exactly one code bit: setting
     # one stored bit changes exactly one code, by exactly one power of two.
@@ -151,7 +162,7 @@ def test_codebook_layout_is_a_bijection(bits):
     assert len(seen) == 32 * bits
 
 
-@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("bits", [2, 3, 6])
 def test_codebook_roundtrip_exact_weights(bits):
     # Weights that the format represents exactly: w = LUT[c] * s. Encode by
     # nearest entry, pack independently, decode with the oracle: bitwise equal.
@@ -251,6 +262,9 @@ LAYER_SHAPES = [
     small_workload("cb_b", 6, 3, 256, 256, bits_mix="alternate", config_id=202),
     small_workload("cb_c", 4, 2, 384, 128, bits_mix="alternate", config_id=203),
     small_workload("fp4", 6, 2, 256, 128, fmt="nvfp4", bits_mix="nvfp4", config_id=204),
+    # with an always-on shared expert (6-bit, and 2-bit for a second width)
+    small_workload("sh6", 6, 2, 256, 128, bits_mix="alternate", config_id=205, shared_bits=6),
+    small_workload("sh2", 8, 3, 256, 256, bits_mix="all2", config_id=206, shared_bits=2),
 ]
 
 
@@ -268,6 +282,20 @@ def test_tiny_workload_matches_brute_force():
     r = oracle.Layer.from_case(case).run(case["x"], case["logits"])
     ref = brute.layer_plain(case)
     assert np.max(np.abs(r["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_shared_expert_adds_its_ffn_with_weight_one():
+    # The shared expert's output is added with weight 1 to every token: the
+    # difference between the layer with and without it is that expert's FFN,
+    # here computed by the plain-basis brute force on its own.
+    w = LAYER_SHAPES[4]
+    case = gen.make_case(w, 3)
+    with_sh = oracle.Layer.from_case(case).run(case["x"], case["logits"])["out"]
+    no_sh = oracle.Layer.from_case(dict(case, shared=None, shared_bits=0)).run(
+        case["x"], case["logits"])["out"]
+    only = brute.shared_plain(case)
+    assert np.max(np.abs((with_sh - no_sh) - only)) <= 1e-12 * np.max(np.abs(only))
+    assert np.max(np.abs(only)) > 0
 
 
 @pytest.mark.parametrize("fmt", ["codebook", "nvfp4"])
