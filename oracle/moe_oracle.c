@@ -169,7 +169,10 @@ void orc_unrotate(int n, const int8_t *signs, const double *in, double *out)
  *   K = 6:           the slot read as one 192-bit little-endian string:
  *                    bits 6 jj .. 6 jj + 5 (word q div 32, bit q mod 32 for
  *                    string bit q).
- * Every bit of the K words holds exactly one code bit. */
+ * Every bit of the K words holds exactly one code bit.
+ * Word d of slot l of tile tau lies at word tau*64*K + l*K + d, except for
+ * K = 6, whose tiles hold words 0..2 of the 64 slots, then words 3..5:
+ * tau*384 + (d div 3)*192 + l*3 + d mod 3. */
 static void codebook_bit_positions(int bits, int jj, int word[6], int bit[6])
 {
     int k;
@@ -211,12 +214,14 @@ uint32_t orc_codebook_code(int bits, int N, int C, const uint32_t *codes, int n,
     int q = cc / 32, jj = cc % 32;
     int slot = q * 16 + r;
     long tau = (long)rb * G + g;
-    const uint32_t *w = codes + (tau * 64 + slot) * bits;
     int word[6], bit[6], k;
     uint32_t code = 0;
     codebook_bit_positions(bits, jj, word, bit);
-    for (k = 0; k < bits; ++k)
-        code |= ((w[word[k]] >> bit[k]) & 1u) << k;
+    for (k = 0; k < bits; ++k) {
+        long at = bits == 6 ? tau * 384 + (word[k] / 3) * 192 + slot * 3 + word[k] % 3
+                            : (tau * 64 + slot) * bits + word[k];
+        code |= ((codes[at] >> bit[k]) & 1u) << k;
+    }
     return code;
 }
 

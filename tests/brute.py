@@ -85,10 +85,19 @@ def _slot_bit_tables(bits):
     return tab
 
 
+def _slot_words(words, bits, ntiles):
+    """[tile, slot, word] view of the stored words: slot-major, except that a
+    6-bit tile holds words 0..2 of its 64 slots, then words 3..5."""
+    w = np.asarray(words, np.uint32)
+    if bits == 6:
+        return w.reshape(ntiles, 2, 64, 3).transpose(0, 2, 1, 3).reshape(ntiles, 64, 6)
+    return w.reshape(ntiles, 64, bits)
+
+
 def codebook_codes(words, bits, N, C):
     """Code matrix [N, C] from the tiled stored words (numpy.unpackbits)."""
     RB, G = N // 16, C // 128
-    w = np.asarray(words, np.uint32).reshape(RB * G, 64, bits)
+    w = np.ascontiguousarray(_slot_words(words, bits, RB * G))
     b = np.unpackbits(w.view(np.uint8).reshape(RB * G, 64, bits, 4), axis=-1, bitorder="little")
     b = b.reshape(RB * G, 64, bits, 32)  # [tile, slot, word, bit]
     codes = np.zeros((RB * G, 64, 32), np.int64)
@@ -111,7 +120,10 @@ def pack_codebook(codes, bits):
         for sig, (wd, bt) in enumerate(entry):
             b[:, :, wd, bt] = (c5[:, :, jj] >> sig) & 1
     by = np.packbits(b.reshape(RB * G, 64, bits, 4, 8), axis=-1, bitorder="little")
-    return by.reshape(-1).view(np.uint32).copy()
+    w = by.reshape(RB * G, 64, bits * 4).view(np.uint32)          # [tile, slot, word]
+    if bits == 6:
+        w = w.reshape(RB * G, 64, 2, 3).transpose(0, 2, 1, 3)     # [tile, half, slot, word]
+    return np.ascontiguousarray(w).reshape(-1).copy()
 
 
 def codebook_scales(scales, N, C):

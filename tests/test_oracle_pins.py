@@ -135,10 +135,14 @@ def test_codebook_layout_hand_values():
     # K = 6: column jj at bits 6 jj .. 6 jj + 5 of the slot's 192-bit string.
     # Column 0 = bits 0-5 of word 0; column 5 straddles words 0 and 1 (bits 30,
     # 31 of word 0 are its code bits 0, 1); column 31 = bits 26-31 of word 5.
+    # A 6-bit tile holds words 0..2 of its 64 slots, then words 3..5: word d of
+    # slot 0 is stored word (d div 3) * 192 + d mod 3.
     w6 = np.zeros(N * C * 6 // 32, np.uint32)
     w6[0] = 0x8000002A             # column 0 = 0b101010 = 42; word 0 bit 31 -> column 5 bit 1
     w6[1] = 0x00000005             # word 1 bits 0, 2 -> column 5 bits 2, 4
-    w6[5] = 0xFC000000             # column 31 = 63
+    w6[192 + 2] = 0xFC000000       # slot 0 word 5: column 31 = 63
+    w6[3 * 17] = 0x00000001        # slot 17 (row 1, cols 32..63) word 0: col 32 = 1
+    assert oracle.codebook_code(6, N, C, w6, 1, 32) == 1
     got = [oracle.codebook_code(6, N, C, w6, 0, c) for c in range(128)]
     want = [0] * 128
     want[0], want[5], want[31] = 42, 2 + 4 + 16, 63
@@ -154,7 +158,10 @@ def test_codebook_layout_is_a_bijection(bits):
     for d in range(bits):
         for bit in range(32):
             words = np.zeros(N * C * bits // 32, np.uint32)
-            words[d] = np.uint32(1 << bit)   # slot 0: row 0, columns 0..31
+            # word d of slot 0 (row 0, columns 0..31); a 6-bit tile stores
+            # words 0..2 of its slots, then words 3..5
+            at = (d // 3) * 192 + d % 3 if bits == 6 else d
+            words[at] = np.uint32(1 << bit)
             codes = [oracle.codebook_code(bits, N, C, words, 0, c) for c in range(32)]
             nz = [(c, v) for c, v in enumerate(codes) if v]
             assert len(nz) == 1 and bin(nz[0][1]).count("1") == 1, (d, bit, nz)
