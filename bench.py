@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack43",
-                    choices=["stack43", "pack46", "full_layer", "rank_share", "nvfp4", "tiny"])
+                    choices=["stack43", "pack46", "stack43_shared", "shared_layer", "full_layer",
+                             "rank_share", "nvfp4", "tiny"])
     ap.add_argument("--m", type=int, default=None, help="tokens per step (default: workload's)")
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the stack (default: the workload's, 43 for stack43)")
@@ -128,7 +129,7 @@ def main():
     from moe_synth import WORKLOADS, gen
 
     w = WORKLOADS[args.workload]
-    m = args.m or (16 if args.workload in ("stack43", "full_layer") else w.max_tokens)
+    m = args.m or (16 if args.workload in ("stack43", "full_layer", "shared_layer") else w.max_tokens)
     n_layers = args.layers or w.layers
     stacked = n_layers > 1
     dev = torch.device("cuda")
@@ -168,6 +169,8 @@ def main():
         b = layer.buckets(m)
         experts = np.nonzero(b["counts"])[0]
         hit.append(len(experts))
+        if layer.has_shared:  # the shared expert (stored as expert E) reads its weights too
+            experts = np.append(experts, layer.E)
         weight_bytes.append(layer.weight_bytes(experts))
         st = layer.stats()
         assert st.error_word == 0 and st.items_done == st.items, "expert kernel incomplete"

@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoedecode.so")
 
-MOE_DECODE_ABI_VERSION = 1
+MOE_DECODE_ABI_VERSION = 2
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_HIP, MOE_E_NOMEM, MOE_E_STREAM, MOE_E_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
 MOE_FMT_CODEBOOK, MOE_FMT_NVFP4 = 1, 2
@@ -30,7 +30,8 @@ class moe_decode_config(C.Structure):
     _fields_ = [("abi_version", C.c_uint32), ("format", C.c_int32), ("num_experts", C.c_int32),
                 ("top_k", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32),
                 ("max_tokens", C.c_int32), ("tensors", C.POINTER(moe_tensor_desc)),
-                ("signs_hidden", C.c_void_p), ("signs_inter", C.c_void_p)]
+                ("signs_hidden", C.c_void_p), ("signs_inter", C.c_void_p),
+                ("shared", C.POINTER(moe_tensor_desc))]
 
 
 class moe_decode_info(C.Structure):

@@ -249,14 +249,24 @@ __device__ void bucket_block(const Params &p, int m)
     const int total = packed_total & 0xFFF, nhit = (packed_total >> 12) & 0x3FF,
               ngroups = packed_total >> 22;
     Plan *P = p.plan;
+    // the shared expert (if any) comes first: expert id E, bucket rows
+    // m*k + t for every token t, in row groups of <= 16. It is the largest
+    // expert of the layer (every token, wider codes), so its items start
+    // first and its down items are not the last to find their h.
+    const int ngs = p.has_shared ? (m + kGroupRows - 1) / kGroupRows : 0;
+    if (tid < ngs) {
+        P->g_expert[tid] = E;
+        P->g_off[tid] = m * k + kGroupRows * tid;
+        P->g_rows[tid] = min(kGroupRows, m - kGroupRows * tid);
+    }
     if (tid < E) {
         s_off[tid] = off;
         p.counts[tid] = cnt;
         p.offsets[tid] = off;
         for (int g = 0; g < ng_e; ++g) {
-            P->g_expert[gbase + g] = tid;
-            P->g_off[gbase + g] = off + kGroupRows * g;
-            P->g_rows[gbase + g] = min(kGroupRows, cnt - kGroupRows * g);
+            P->g_expert[ngs + gbase + g] = tid;
+            P->g_off[ngs + gbase + g] = off + kGroupRows * g;
+            P->g_rows[ngs + gbase + g] = min(kGroupRows, cnt - kGroupRows * g);
         }
     }
     __syncthreads();
@@ -268,19 +278,19 @@ __device__ void bucket_block(const Params &p, int m)
     }
     if (tid == 0) {
         p.offsets[E] = total;
-        const int n1 = ngroups * (p.n_rb1 / p.span1) * p.ks1;
+        const int n1 = (ngroups + ngs) * (p.n_rb1 / p.span1) * p.ks1;
         P->m = m;
         P->n_hit = nhit;
-        P->n_groups = ngroups;
+        P->n_groups = ngroups + ngs;
         P->n_items1 = n1;
-        P->n_items = n1 + ngroups * p.n_rb2 * p.ks2;
+        P->n_items = n1 + (ngroups + ngs) * p.n_rb2 * p.ks2;
         for (int i = 0; i < kDoneSlots; ++i)
             p.ctr->items_done[i] = 0;
         p.ctr->error_word = 0;
     }
-    for (int i = tid; i < ngroups * p.n_rb1; i += kRouteThreads)
+    for (int i = tid; i < (ngroups + ngs) * p.n_rb1; i += kRouteThreads)
         p.rb_done[i * kCtrStride] = 0;
-    for (int i = tid; i < ngroups; i += kRouteThreads)
+    for (int i = tid; i < ngroups + ngs; i += kRouteThreads)
         p.h_ready[i * kCtrStride] = 0;
 }
 
@@ -346,10 +356,19 @@ constexpr int kWaveRB = 4;
 constexpr int kExpertThreads = 256;
 constexpr int kExpertWaves = kExpertThreads / 64;
 
+// Kernel classes: the codebook format without and with 6-bit tensors (the
+// 6-bit path is compiled only into the latter, so layers without 6-bit
+// tensors run code that has none of it), and NVFP4.
+constexpr int kClassCb6 = 3;
+template <int CLASS>
+constexpr bool is_cb = CLASS != kFmtNvfp4;
+template <int CLASS>
+constexpr bool has6 = CLASS == kClassCb6;
+
 // Slot words held per tile: codebook up to 3 (2-bit tensors use 2), NVFP4 4.
 template <int CLASS>
 struct Slot {
-    static constexpr int W = CLASS == kFmtCodebook ? 3 : 4;
+    static constexpr int W = is_cb<CLASS> ? 3 : 4;
 };
 
 // Byte tables of the per-tensor codebook for v_perm lookups: tab[0] / tab[1]
@@ -429,6 +448,11 @@ struct WaveJob {
     float ts;
     int bits;
     int G, rb0, g0;
+    // entry i of a 6-bit codebook (i < 64)
+    __device__ __forceinline__ _Float16 lut6(int i) const
+    {
+        return __builtin_bit_cast(_Float16, *(const uint16_t GLOBAL *)(lut + i));
+    }
 };
 
 // One register buffer of weight data: one 128-column group of the wave's
@@ -463,30 +487,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void GLOBAL 
 // flight holds no address registers; one VMEM instruction per tile whatever
 // the bit width, so the waits the compiler places stay exact when the next
 // item's width differs.
+// 6-bit codes: a wave takes 2 tiles per group (kWaveRB / 2); a 6-bit tile
+// stores words 0..2 of its 64 slots, then words 3..5, so a lane's half slots
+// load exactly like a 3-bit slot (lane offset 12 bytes, the half in the
+// scalar offset) into buffer rows 2r (columns 0..15) and 2r + 1 (16..31):
+// same buffer shape, same count of loads, no extra address registers.
 template <int CLASS, int KB>
 __device__ __forceinline__ void load_group(GroupBuf<CLASS> &b, const WaveJob &J, int j, int lane,
                                            int sc_lane)
 {
     const __amdgpu_buffer_rsrc_t rc = tensor_rsrc(J.codes);
     const __amdgpu_buffer_rsrc_t rsc = tensor_rsrc(J.scales);
+    const bool six = has6<CLASS> && J.bits == 6;
     const int g = J.g0 + j;
 #pragma unroll
     for (int i = 0; i < kWaveRB; ++i) {
-        const int tile = (J.rb0 + i) * J.G + g;
-        if constexpr (CLASS == kFmtCodebook) {
-            if (KB == 3 || (KB == 0 && J.bits == 3)) {
-                const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12, tile * 768, 0);
-                b.w[i][0] = v[0];
-                b.w[i][1] = v[1];
-                b.w[i][2] = v[2];
+        const int trow = six ? J.rb0 + (i >> 1) : J.rb0 + i;  // tile row block
+        const int tile = trow * J.G + g;
+        if constexpr (is_cb<CLASS>) {
+            // one load instruction for 3-bit and 6-bit (the width only moves
+            // the scalar offset): separate loads would have to be merged by
+            // register copies, which wait for the loads at once
+            // (the words are merged after the branch and stored once: stores
+            // to different words in the two branches get merged through a
+            // computed address, which sends the buffer to stack memory)
+            uint32_t w0, w1, w2 = b.w[i][2];
+            if (KB == 3 || (KB == 0 && (J.bits == 3 || six))) {
+                const int soff = six ? tile * 1536 + (i & 1) * 768 : tile * 768;
+                const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12, soff, 0);
+                w0 = v[0];
+                w1 = v[1];
+                w2 = v[2];
             } else {
                 const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane * 8, tile * 512, 0);
-                b.w[i][0] = v[0];
-                b.w[i][1] = v[1];
+                w0 = v[0];
+                w1 = v[1];
             }
-            // scales[row][g], row = 16 (rb0 + i) + lane % 16
-            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane,
-                                                           ((J.rb0 + i) * 16 * J.G + g) * 2, 0);
+            b.w[i][0] = w0;
+            b.w[i][1] = w1;
+            b.w[i][2] = w2;
+            // scales[row][g], row = 16 trow + lane % 16
+            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, (trow * 16 * J.G + g) * 2, 0);
         } else {
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, tile * 1024, 0);
             b.w[i][0] = v[0];
@@ -542,17 +583,76 @@ __device__ __forceinline__ void process_group(const GroupBuf<CLASS> &b, int j, c
     }
 }
 
+// Codebooks of 6-bit tensors in LDS, one per pair of waves (waves 0-1 and 2-3
+// compute the same tensor in every item): 64 fp16 entries each.
+constexpr int kLut6Slots = 2;
+__shared__ _Float16 s_lut6[kLut6Slots * 64];
+
+// The 8 fp16 B-operand values of step sp (0 or 1) of a 6-bit half slot: the
+// half's 16 codes are bits 6c .. 6c+5 of w[0..2] read as a 96-bit
+// little-endian string. Each code, shifted to bits 1-6 and or-ed with the
+// wave's codebook base (lbase = 128 x slot), is the byte address of its
+// fp16 entry.
+__device__ __forceinline__ half8 decode6(const uint32_t (&w)[3], int sp, uint32_t lbase)
+{
+    const char *T = (const char *)s_lut6;
+    uint32_t o[4];
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+        _Float16 v[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int q = 6 * (8 * sp + 2 * c2 + e), wd = q >> 5, off = q & 31;
+            uint32_t x;
+            if (off == 0)
+                x = w[wd] << 1;
+            else if (off <= 26)
+                x = w[wd] >> (off - 1);
+            else
+                x = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off - 1);
+            v[e] = *(const _Float16 *)(T + ((x & 0x7Eu) | lbase));
+        }
+        o[c2] = __builtin_bit_cast(uint32_t, half2v{v[0], v[1]});
+    }
+    return __builtin_bit_cast(half8, u32x4{o[0], o[1], o[2], o[3]});
+}
+
+// Group j of a 6-bit item: 2 tiles; steps 0-1 of tile r come from buffer
+// row 2r, steps 2-3 from row 2r + 1. Results accumulate in acc[0], acc[1].
+template <int CLASS>
+__device__ __forceinline__ void process_group6(const GroupBuf<CLASS> &b, int j, const _Float16 *Arow,
+                                               uint32_t lbase, floatx4 (&acc)[kWaveRB])
+{
+    half8 a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a[s] = *(const half8 *)(Arow + j * 128 + s * 8);
+#pragma unroll
+    for (int r = 0; r < kWaveRB / 2; ++r) {
+        floatx4 cc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], decode6(b.w[2 * r + (s >> 1)], s & 1, lbase),
+                                                         cc, 0, 0, 0);
+        const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[2 * r]);
+        acc[r] += f * cc;
+        asm volatile("" : "+v"(acc[r]));
+    }
+}
+
 // Group j of the current item: the codebook bit width is a runtime property
 // of the tensor, dispatched here around the decode and MFMAs only, so the
 // buffers loaded outside stay in the same registers on both paths.
 template <int CLASS>
 __device__ __forceinline__ void process_any(const GroupBuf<CLASS> &b, int j, int bits,
                                             const _Float16 *Arow, const uint32_t (&tab)[4],
-                                            floatx4 (&acc)[kWaveRB])
+                                            uint32_t lbase, floatx4 (&acc)[kWaveRB])
 {
-    if constexpr (CLASS == kFmtCodebook) {
+    if constexpr (is_cb<CLASS>) {
         if (bits == 3)
             process_group<CLASS, 3>(b, j, Arow, tab, acc);
+        else if (has6<CLASS> && bits == 6)
+            process_group6<CLASS>(b, j, Arow, lbase, acc);
         else
             process_group<CLASS, 2>(b, j, Arow, tab, acc);
     } else {
@@ -567,12 +667,12 @@ __device__ __forceinline__ void process_any(const GroupBuf<CLASS> &b, int j, int
 template <int CLASS, int NG, typename After>
 __device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
                                               const _Float16 *Arow, const uint32_t (&tab)[4],
-                                              floatx4 (&acc)[kWaveRB], After &after)
+                                              uint32_t lbase, floatx4 (&acc)[kWaveRB], After &after)
 {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
         GroupBuf<CLASS> &b = (j & 1) ? bB : bA;
-        process_any<CLASS>(b, j, bits, Arow, tab, acc);
+        process_any<CLASS>(b, j, bits, Arow, tab, lbase, acc);
         after(j, b);
     }
 }
@@ -648,7 +748,7 @@ __device__ __forceinline__ DescRaw load_desc(const Params &p, const Item &it, in
 // The matrix part wave `wave` computes for item `it`: a gate/up item's 128
 // rows of gate and of up go to the two halves of the waves, a down item's 256
 // rows to all waves, kWaveRB row blocks of 16 each.
-template <int NG>
+template <int CLASS, int NG>
 __device__ __forceinline__ WaveJob make_job(const Params &p, const DescRaw &d, const Item &it,
                                             int wave)
 {
@@ -660,8 +760,10 @@ __device__ __forceinline__ WaveJob make_job(const Params &p, const DescRaw &d, c
     J.ts = __uint_as_float((uint32_t)uniform((int)d.d1[2]));
     J.bits = uniform((int)d.d1[3]);
     J.G = it.down ? p.I / 128 : p.H / 128;
-    J.rb0 = it.down ? it.rb * 16 + wave * kWaveRB
-                    : it.rb * 8 + (wave % (kExpertWaves / 2)) * kWaveRB;
+    // a 6-bit wave takes kWaveRB / 2 tiles per row block unit (see load_group)
+    const int per_wave = has6<CLASS> && J.bits == 6 ? kWaveRB / 2 : kWaveRB;
+    J.rb0 = it.down ? it.rb * 16 + wave * per_wave
+                    : it.rb * 8 + (wave % (kExpertWaves / 2)) * per_wave;
     J.g0 = it.kq * NG;
     return J;
 }
@@ -808,17 +910,24 @@ struct Stage {
 // Store the partial sums of one row block of an item (rows rb0.. of job J).
 // Gate/up partials go out agent-coherent for the finishing block; down
 // partials are read only by the combine kernel, after this kernel ends.
+template <int CLASS>
 __device__ __forceinline__ void store_rows(const Params &p, const Item &it, const WaveJob &J,
                                            const floatx4 (&acc)[kWaveRB])
 {
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
+    // the lane index, opaque to the compiler: the addresses below are
+    // recomputed at each call instead of being hoisted to the kernel start
+    // and held (or spilled) across the whole item loop
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
     const int proj = item_proj(it, tid >> 6);
+    const int ntiles = has6<CLASS> && J.bits == 6 ? kWaveRB / 2 : kWaveRB;  // 6-bit: 2 per wave
 #pragma unroll
     for (int i = 0; i < kWaveRB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int tok = 4 * (lane >> 4) + j;
-            if (tok < it.R) {
+            if (i < ntiles && tok < it.R) {
                 const size_t row = (size_t)it.kq * p.pair_cap + it.off + tok;
                 const int n = (J.rb0 + i) * 16 + (lane & 15);
                 if (it.down)
@@ -899,11 +1008,15 @@ void expert_kernel(Params p)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = uniform(tid >> 6);
     const int r16 = lane & 15, q = lane >> 4;
+    // 6-bit codebook slot: the waves of one gate/up half (same tensor in every item)
+    const uint32_t lut_slot = (uint32_t)(wave / (kExpertWaves / kLut6Slots));
     const int m = uniform(P->m), n_items = uniform(P->n_items), n_items1 = uniform(P->n_items1);
     const int n_groups = uniform(P->n_groups);
 
-    for (int i = tid; i < m * p.k; i += kExpertThreads)
-        s_tok[i] = p.rows[i] / p.k;
+    // token of each bucket row: routed rows from the row list, then the
+    // shared expert's row m*k + t of token t
+    for (int i = tid; i < m * (p.k + p.has_shared); i += kExpertThreads)
+        s_tok[i] = i < m * p.k ? p.rows[i] / p.k : i - m * p.k;
     for (int i = tid; i < n_groups; i += kExpertThreads) {
         s_grp.expert[i] = P->g_expert[i];
         s_grp.off[i] = P->g_off[i];
@@ -917,12 +1030,14 @@ void expert_kernel(Params p)
     if (cur.valid) {
         GroupBuf<CLASS> bA, bB;
         int sb = 0;  // row block of cur's span being computed
-        WaveJob J = make_job<NG>(p, load_desc(p, cur, wave), cur, wave);
+        WaveJob J = make_job<CLASS, NG>(p, load_desc(p, cur, wave), cur, wave);
         uint32_t tab[4] = {0, 0, 0, 0};
 
         while (true) {
-            const bool last = sb + 1 == cur.span;
-            const int sc_lane = CLASS == kFmtCodebook ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+            // 6-bit items: each row block takes two units of half the rows
+            const int six = (has6<CLASS> && J.bits == 6) ? 1 : 0;
+            const bool last = sb + 1 == (cur.span << six);
+            const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
             // after the item's last row block comes the next item: its plan
             // entries (LDS) and descriptor (vector loads)
             const int nxt_ticket = ticket + (int)gridDim.x;
@@ -944,21 +1059,30 @@ void expert_kernel(Params p)
                 St st;
                 st.issue(p, cur, s_tok);
                 u32x4 lut = u32x4{0, 0, 0, 0};
-                if constexpr (CLASS == kFmtCodebook)
+                _Float16 lut6 = 0;
+                if constexpr (is_cb<CLASS>) {
                     lut = load_lut_raw(J);
+                    if (has6<CLASS> && J.bits == 6)
+                        lut6 = J.lut6(lane);
+                }
                 load_group<CLASS, 0>(bA, J, 0, lane, sc_lane);
                 st.commit(cur, Abuf);
                 if constexpr (NG > 1)
                     load_group<CLASS, 0>(bB, J, 1, lane, sc_lane);
+                // a 6-bit codebook goes to the wave pair's LDS slot (the waves
+                // sharing it write the same values), after the group loads so
+                // that waiting for it does not wait for them
+                if (has6<CLASS> && J.bits == 6)
+                    s_lut6[lut_slot * 64 + lane] = lut6;
                 __syncthreads();
-                if constexpr (CLASS == kFmtCodebook)
+                if constexpr (is_cb<CLASS>)
                     lut_tables(lut, tab);
             }
             // after group j, the freed buffer takes this row block's group
             // j+2, else group j+2-NG of the span's next row block (same
             // activations and tensor: no staging in between)
             WaveJob JN = J;
-            JN.rb0 += (cur.down ? 16 : 8);
+            JN.rb0 += (cur.down ? 16 : 8) >> six;
             auto after = [&](int j, GroupBuf<CLASS> &b) {
                 const int nx = NG == 1 ? 0 : j + 2 - NG;
                 if (NG > 1 && j + 2 < NG)
@@ -971,13 +1095,13 @@ void expert_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < kWaveRB; ++i)
                 acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, acc, after);
-            if constexpr (CLASS != kFmtCodebook)
+            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, lut_slot * 128u, acc, after);
+            if constexpr (!is_cb<CLASS>)
 #pragma unroll
                 for (int i = 0; i < kWaveRB; ++i)
                     acc[i] *= J.ts;
             if (ok)
-                store_rows(p, cur, J, acc);
+                store_rows<CLASS>(p, cur, J, acc);
             if (!last) {
                 ++sb;
                 J = JN;
@@ -992,7 +1116,7 @@ void expert_kernel(Params p)
             ticket = nxt_ticket;
             cur = nxt;
             sb = 0;
-            J = make_job<NG>(p, dn, nxt, wave);
+            J = make_job<CLASS, NG>(p, dn, nxt, wave);
         }
     }
     if (tid == 0 && done)
@@ -1004,7 +1128,8 @@ void expert_kernel(Params p)
 // ---------------------------------------------------------------------------
 
 // out[t][n] = sum_j w[t][j] * sum_s y_part[s][pos(t, j)][n], slots j in
-// order, splits s in order (no float atomics: bitwise reproducible). Block
+// order, splits s in order (no float atomics: bitwise reproducible), plus
+// the shared expert's row (weight 1) when there is one. Block
 // (rb, t) covers rows rb*256 .. +255 of token t; runs after the expert
 // kernel, so plain loads see its partial sums.
 __global__ __launch_bounds__(256) void combine_kernel(Params p)
@@ -1050,6 +1175,15 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p)
             if (j0 + jj < p.k)
                 o += wj[jj] * y[jj];
     }
+    if (p.has_shared) {
+        // the shared expert's row of token t (bucket row m*k + t), weight 1,
+        // after the routed slots
+        const size_t q = (size_t)gridDim.y * p.k + t;
+        float ysh = 0.0f;
+        for (int s = 0; s < p.ks2; ++s)
+            ysh += p.y_part[((size_t)s * p.pair_cap + q) * p.H + row];
+        o += ysh;
+    }
     p.out[(size_t)t * p.H + row] = o;
 }
 
@@ -1072,10 +1206,18 @@ static void *expert_fn()
     return (void *)expert_kernel<CLASS, NG>;
 }
 
-// The expert kernel specialised for the format class and the groups per
-// column split (1, 2, 4 or 8).
-static void *expert_kernel_for(int format, int ng)
+// The expert kernel specialised for the format class (codebook with or
+// without 6-bit tensors, NVFP4) and the groups per column split (1, 2, 4, 8).
+static void *expert_kernel_for(int format, int ng, bool six)
 {
+    if (format == kFmtCodebook && six) {
+        switch (ng) {
+        case 8: return expert_fn<kClassCb6, 8>();
+        case 4: return expert_fn<kClassCb6, 4>();
+        case 2: return expert_fn<kClassCb6, 2>();
+        default: return expert_fn<kClassCb6, 1>();
+        }
+    }
     if (format == kFmtCodebook) {
         switch (ng) {
         case 8: return expert_fn<kFmtCodebook, 8>();
@@ -1100,14 +1242,15 @@ hipError_t launch_combine(const Params &p, int m, hipStream_t s)
 
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s)
 {
-    void *fn = expert_kernel_for(p.format, p.kc1 / 128);
+    void *fn = expert_kernel_for(p.format, p.kc1 / 128, p.has6 != 0);
     void *args[] = {const_cast<Params *>(&p)};
     return hipLaunchKernel(fn, dim3(grid), dim3(kExpertThreads), args, lds_bytes, s);
 }
 
-hipError_t expert_occupancy(int format, int ng, int *blocks_per_cu, size_t lds_bytes)
+hipError_t expert_occupancy(int format, int ng, bool six, int *blocks_per_cu, size_t lds_bytes)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, expert_kernel_for(format, ng),
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
+                                                        expert_kernel_for(format, ng, six),
                                                         kExpertThreads, lds_bytes);
 }
 

@@ -107,18 +107,23 @@ static moe_status validate(const moe_decode_config *c)
     const bool cb = c->format == MOE_FMT_CODEBOOK;
     if (cb && (!c->signs_hidden || !c->signs_inter))
         return fail(MOE_E_INVALID, "codebook format needs signs_hidden and signs_inter");
-    for (int e = 0; e < c->num_experts; ++e) {
-        const int b0 = c->tensors[3 * e].bits;
+    if (c->shared && !cb)
+        return fail(MOE_E_UNSUPPORTED, "a shared expert needs the codebook format");
+    const int n_exp = c->num_experts + (c->shared ? 1 : 0);
+    for (int e = 0; e < n_exp; ++e) {
+        // expert e == num_experts is the shared expert
+        const moe_tensor_desc *td = e < c->num_experts ? c->tensors + 3 * e : c->shared;
+        const int b0 = td[0].bits;
         for (int p = 0; p < 3; ++p) {
-            const moe_tensor_desc &t = c->tensors[3 * e + p];
+            const moe_tensor_desc &t = td[p];
             if (!t.codes || !t.scales)
                 return fail(MOE_E_INVALID, "expert %d projection %d: NULL codes or scales", e, p);
             if (t.bits != b0)
                 return fail(MOE_E_INVALID, "expert %d: projections have different bits", e);
             if (cb) {
-                if (t.bits != 2 && t.bits != 3)
-                    return fail(MOE_E_INVALID, "expert %d projection %d: bits %d not 2 or 3", e, p,
-                                t.bits);
+                if (t.bits != 2 && t.bits != 3 && t.bits != 6)
+                    return fail(MOE_E_INVALID, "expert %d projection %d: bits %d not 2, 3 or 6", e,
+                                p, t.bits);
                 if (!t.lut)
                     return fail(MOE_E_INVALID, "expert %d projection %d: NULL lut", e, p);
                 if (!aligned(t.codes, 16) || !aligned(t.scales, 16) || !aligned(t.lut, 4))
@@ -161,7 +166,13 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.span1 = 1;
     p.n_rb1 = p.I / 128;
     p.n_rb2 = p.H / 256;
-    p.pair_cap = p.max_tokens * p.k;
+    p.has_shared = cfg->shared ? 1 : 0;
+    p.has6 = 0;
+    for (int i = 0; i < 3 * p.E; ++i)
+        p.has6 |= cfg->tensors[i].bits == 6;
+    for (int i = 0; cfg->shared && i < 3; ++i)
+        p.has6 |= cfg->shared[i].bits == 6;
+    p.pair_cap = p.max_tokens * (p.k + p.has_shared);
     p.spin_limit = 2u * 1000u * 1000u;  // polls of up to ~1 us: a ~2 s bound
     p.signs_h = cfg->signs_hidden;
     p.signs_i = cfg->signs_inter;
@@ -190,7 +201,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
         off += (bytes + 255) & ~size_t(255);
         return o;
     };
-    const size_t o_tensors = take(sizeof(DevTensor) * E * 3);
+    const size_t o_tensors = take(sizeof(DevTensor) * (E * 3 + 3));
     const size_t o_ids = take(4 * PC), o_wts = take(4 * PC), o_counts = take(4 * E),
                  o_offsets = take(4 * (E + 1)), o_rows = take(4 * PC), o_pos = take(4 * PC);
     const size_t o_plan = take(sizeof(Plan));
@@ -222,12 +233,13 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.hr = (_Float16 *)(base + o_hr);
     p.y_part = (float *)(base + o_y);
 
-    std::vector<DevTensor> tab(E * 3);
-    for (size_t i = 0; i < E * 3; ++i) {
-        const moe_tensor_desc &t = cfg->tensors[i];
+    std::vector<DevTensor> tab(E * 3 + 3, DevTensor{});
+    for (size_t i = 0; i < E * 3 + (cfg->shared ? 3 : 0); ++i) {
+        const moe_tensor_desc &t = i < E * 3 ? cfg->tensors[i] : cfg->shared[i - E * 3];
         tab[i] = DevTensor{t.codes, t.scales, (const uint16_t *)t.lut, t.tensor_scale, t.bits};
     }
-    err = hipMemcpy(h->dev_tensors, tab.data(), sizeof(DevTensor) * E * 3, hipMemcpyHostToDevice);
+    err = hipMemcpy(h->dev_tensors, tab.data(), sizeof(DevTensor) * (E * 3 + 3),
+                    hipMemcpyHostToDevice);
     if (err == hipSuccess)
         err = hipMemset(base + o_ids, 0, ctr_end - o_ids);
     if (err == hipSuccess)
@@ -250,7 +262,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
         h->span1[m] = (m >= 8 && p.n_rb1 % 2 == 0) ? 2 : 1;
         const size_t lds = (size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) * sizeof(_Float16);
         int bpc = 0;
-        err = expert_occupancy(p.format, p.kc1 / 128, &bpc, lds);
+        err = expert_occupancy(p.format, p.kc1 / 128, p.has6 != 0, &bpc, lds);
         if (err != hipSuccess || bpc < 1)
             return cleanup(fail(MOE_E_UNSUPPORTED, "expert kernel cannot be resident with %zu B LDS",
                                 lds));

@@ -10,7 +10,8 @@ constexpr int kThreads = 256;       // every kernel: 4 wave64s
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxTokens = 32;
-constexpr int kMaxPairs = kMaxTokens * kMaxTopK;
+// Bucket rows: k routed rows per token, plus one per token for a shared expert.
+constexpr int kMaxPairs = kMaxTokens * (kMaxTopK + 1);
 constexpr int kGroupRows = 16;      // rows of one MFMA token block
 // Row groups: each hit expert's bucket split into groups of <= 16 rows.
 constexpr int kMaxGroups = kMaxExperts + kMaxPairs / kGroupRows;
@@ -68,17 +69,20 @@ struct Params {
     int32_t span1;         // gate/up: 128-row blocks per work item (set per run)
     int32_t n_rb1;         // I / 128 gate/up row blocks of 128 (one rotation block each)
     int32_t n_rb2;         // H / 256 down row blocks of 256
-    int32_t pair_cap;      // max_tokens * k
+    int32_t pair_cap;      // bucket row capacity: max_tokens * (k + has_shared)
+    int32_t has6;          // 1: some tensor has 6-bit codes (selects the kernel with that path)
+    int32_t has_shared;    // 1: an always-on shared expert (tensors 3E..3E+2, bucket
+                           // rows m*k + t, group expert id E)
     uint32_t spin_limit;   // polls before a dependency wait gives up
     float *out;            // [m][H] result of the current launch
-    const DevTensor *tensors;   // [E*3]
+    const DevTensor *tensors;   // [E*3 + 3] (the last three: the shared expert)
     const int8_t *signs_h;      // [H]
     const int8_t *signs_i;      // [I]
     int32_t *ids;          // [pair_cap] expert of (t, j)
     float *wts;            // [pair_cap] router weight of (t, j)
     int32_t *counts;       // [E]
     int32_t *offsets;      // [E+1]
-    int32_t *rows;         // [pair_cap] bucket row list, entry t*k+j
+    int32_t *rows;         // [pair_cap] bucket row list, entry t*k+j (routed rows)
     int32_t *pos;          // [pair_cap] bucket position of (t, j)
     Plan *plan;
     _Float16 *xr;          // [max_tokens][H] rotated activations (fp16)
@@ -97,6 +101,6 @@ hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits,
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const Params &p, int m, hipStream_t s);
 // Occupancy of the expert kernel for a given dynamic LDS size.
-hipError_t expert_occupancy(int format, int ng, int *blocks_per_cu, size_t lds_bytes);
+hipError_t expert_occupancy(int format, int ng, bool six, int *blocks_per_cu, size_t lds_bytes);
 
 }  // namespace moe

@@ -36,16 +36,24 @@ class DeviceLayer:
     """One MoE layer resident on the GPU plus its moe_decode handle.
 
     fmt: "codebook" | "nvfp4"; tensors: {(e, proj): dict(codes, scales, lut,
-    tensor_scale, bits)} for every expert; signs: int8 arrays (codebook).
+    tensor_scale, bits)} for every expert; signs: int8 arrays (codebook);
+    shared: None or {proj: tensor} of the always-on shared expert (stored
+    after the routed experts, passed as the config's `shared` descriptors).
     """
 
     def __init__(self, fmt, num_experts, top_k, hidden, inter, tensors, signs_hidden=None,
-                 signs_inter=None, max_tokens=24, device="cuda"):
+                 signs_inter=None, max_tokens=24, device="cuda", shared=None):
         E = num_experts
         keys = [(e, p) for e in range(E) for p in range(3)]
         missing = [k for k in keys if k not in tensors]
         if missing:
             raise ValueError(f"missing stored tensors for {missing[:4]}...")
+        n_routed = len(keys)
+        if shared:
+            tensors = dict(tensors)
+            for p in range(3):
+                tensors[(E, p)] = shared[p]
+            keys = keys + [(E, p) for p in range(3)]
         self.codes, co = _blob([tensors[k]["codes"] for k in keys], device)
         self.scales, so = _blob([tensors[k]["scales"] for k in keys], device)
         luts = [tensors[k]["lut"] for k in keys]
@@ -53,7 +61,7 @@ class DeviceLayer:
             self.luts, lo = _blob(luts, device)
         else:
             self.luts, lo = None, [None] * len(keys)
-        descs = (moe_tensor_desc * (3 * E))()
+        descs = (moe_tensor_desc * len(keys))()
         for i, k in enumerate(keys):
             t = tensors[k]
             descs[i].codes = self.codes.data_ptr() + co[i]
@@ -66,11 +74,14 @@ class DeviceLayer:
         if signs_hidden is not None:
             self.sh = torch.from_numpy(np.ascontiguousarray(signs_hidden, np.int8)).to(device)
             self.si = torch.from_numpy(np.ascontiguousarray(signs_inter, np.int8)).to(device)
+        shared_ptr = (C.cast(C.byref(descs, n_routed * C.sizeof(moe_tensor_desc)),
+                             C.POINTER(moe_tensor_desc)) if shared else None)
         self.cfg = moe_decode_config(
             MOE_DECODE_ABI_VERSION, MOE_FMT_CODEBOOK if fmt == "codebook" else MOE_FMT_NVFP4,
             E, top_k, hidden, inter, max_tokens, C.cast(descs, C.POINTER(moe_tensor_desc)),
             None if self.sh is None else self.sh.data_ptr(),
-            None if self.si is None else self.si.data_ptr())
+            None if self.si is None else self.si.data_ptr(), shared_ptr)
+        self.has_shared = bool(shared)
         self.fmt, self.E, self.k, self.H, self.I = fmt, E, top_k, hidden, inter
         self.max_tokens = max_tokens
         self.device = device
@@ -81,7 +92,8 @@ class DeviceLayer:
         w = case["workload"]
         return cls(w.fmt, w.num_experts, w.top_k, w.hidden, w.inter, case["tensors"],
                    case["signs_hidden"], case["signs_inter"],
-                   max_tokens or max(case.get("m", 1), w.max_tokens), device)
+                   max_tokens or max(case.get("m", 1), w.max_tokens), device,
+                   shared=case.get("shared"))
 
     def weight_bytes(self, experts):
         """Stored bytes (codes + scales + codebook) of the given experts."""

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 1u
+#define MOE_DECODE_ABI_VERSION 2u
 
 typedef struct moe_decode_s *moe_decode_t; /* opaque handle, owned by the library */
 
@@ -60,16 +60,20 @@ typedef enum { MOE_FMT_CODEBOOK = 1, MOE_FMT_NVFP4 = 2 } moe_format;
  * tile has 64 slots, slot l covering row 16rb + (l mod 16) and the columns
  * 128g + 32(l div 16) + jj, jj = 0..31, slots in order.
  *
- * MOE_FMT_CODEBOOK (bits = 2 or 3): stand-in for the 2/3-bit codes that the
- * pages name but do not define (page "lna-lab/README.md", "What is in the
- * pack"). Weights live in the rotated basis (see signs_* below).
+ * MOE_FMT_CODEBOOK (bits = 2, 3 or 6): stand-in for the 2/3-bit codes of the
+ * routed experts and the 6-bit codes of the dense linears that the pages
+ * name but do not define (page "lna-lab/README.md", "What is in the pack").
+ * Weights live in the rotated basis (see signs_* below).
  *   codes  : uint32 words, bits words per slot (tile = 64*bits words),
  *            4-byte aligned. Column jj of a slot, code bits LSB first:
  *            bits = 2 (d = jj/16, kk = jj%16): word d, bits 8(kk%4) + 2(kk/4)
  *            and +1. bits = 3, jj < 24 (d = jj/8, i = jj%8): word d, bits
  *            8(i%4) + 3(i/4) + 0..2; jj >= 24 (i = jj-24): bits 0 and 1 at
  *            word i/4, bits 8(i%4) + 6 and + 7, bit 2 at word 2, bit
- *            8(i%4) + 6 + i/4.
+ *            8(i%4) + 6 + i/4. bits = 6: bits 6jj .. 6jj+5 of the slot's six
+ *            words read as one 192-bit little-endian string; a 6-bit tile
+ *            stores words 0..2 of its 64 slots (in slot order), then words
+ *            3..5.
  *   scales : fp16, one per (row, 128-column group), row-major:
  *            scales[n*(C/128) + c/128]. 16-byte aligned.
  *   lut    : fp16[2^bits] codebook. W[n][c] = lut[code] * scale.
@@ -104,6 +108,13 @@ typedef struct {
                                         copied at create */
     const int8_t *signs_hidden;      /* device int8 [H] of +1/-1 (codebook; NULL for NVFP4) */
     const int8_t *signs_inter;       /* device int8 [I] of +1/-1 (codebook; NULL for NVFP4) */
+    const moe_tensor_desc *shared;   /* host [3] gate, up, down of an always-on shared expert
+                                        (codebook format, any codebook bits, the routed
+                                        experts' shapes), or NULL; copied at create. Every
+                                        token runs it; its output is added with weight 1
+                                        after the k routed terms. The pages' MoE block has
+                                        shared experts stored 6-bit with the dense linears
+                                        (page "lna-lab/README.md", "What is in the pack"). */
 } moe_decode_config;
 
 /*

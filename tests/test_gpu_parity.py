@@ -121,6 +121,65 @@ def test_pack_layers_sampled(layer):
         dl.close()
 
 
+SHARED = [
+    (small_workload("sh6a", 8, 2, 256, 128, bits_mix="alternate", config_id=311, shared_bits=6), 1),
+    (small_workload("sh6b", 16, 4, 512, 256, bits_mix="alternate", config_id=312, shared_bits=6), 5),
+    (small_workload("sh6c", 16, 3, 1024, 384, bits_mix="all3", config_id=313, shared_bits=6), 16),
+    (small_workload("sh6d", 32, 4, 512, 256, bits_mix="alternate", config_id=314, shared_bits=6), 24),
+    (small_workload("sh2", 16, 2, 512, 128, bits_mix="all2", config_id=315, shared_bits=2), 17),
+    (small_workload("sh3", 8, 2, 768, 256, bits_mix="all3", config_id=316, shared_bits=3), 3),
+]
+
+
+@pytest.mark.parametrize("w,m", SHARED, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_shared_expert_small(w, m):
+    # The always-on shared expert (6-bit, and 2/3-bit) folded into the launch:
+    # every output element against the oracle, ragged token counts (1..24,
+    # one or two shared row groups).
+    parity(gen.make_case(w, m))
+
+
+@pytest.mark.parametrize("m", [1, 16, 24])
+def test_shared_layer_sampled(m):
+    w = WORKLOADS["shared_layer"]
+    case = gen.make_case(w, m)
+    tokens = sorted(set([0, m // 2, m - 1]))
+    say(f"[parity] shared_layer m={m}")
+    dl = DeviceLayer.from_case(case, max_tokens=24)
+    try:
+        out = run_gpu(dl, case)
+        check_routing(dl, case, m)
+        st = dl.stats()
+        assert st.error_word == 0 and st.items_done == st.items
+        ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+        err = rel_err(out, ref["out"], tokens)
+        say(f"    rel={err:.3e} hit={st.hit_experts} items={st.items}")
+        assert err <= REL_TOL
+    finally:
+        dl.close()
+
+
+def test_shared_expert_bitwise_repeatable():
+    w = small_workload("shrep", 16, 4, 1024, 256, bits_mix="alternate", config_id=317, shared_bits=6)
+    case = gen.make_case(w, 19)
+    say("[bitwise] shared expert, 6 runs")
+    s = torch.cuda.Stream()
+    layer = DeviceLayer.from_case(case, max_tokens=24)
+    try:
+        x, lg, out = to_dev(case)
+        outs = []
+        with torch.cuda.stream(s):
+            for _ in range(6):
+                out.fill_(float("nan"))
+                layer.run(x, lg, out, stream=s)
+                s.synchronize()
+                outs.append(out.clone())
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    finally:
+        layer.close()
+
+
 def test_bitwise_repeatable_and_graph_replay():
     w = small_workload("rep", 16, 4, 1024, 256, bits_mix="alternate", config_id=301)
     case = gen.make_case(w, 24)
