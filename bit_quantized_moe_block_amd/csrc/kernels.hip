@@ -30,6 +30,18 @@
 
 namespace moe {
 
+// Work items of one shared-expert row group in the gate/up (down = false) or
+// down phase: column splits x row blocks, or x half row blocks when its items
+// cover half row blocks.
+__device__ __forceinline__ int shared_items(const Params &p, bool down)
+{
+    const int ks = down ? p.ks2 : p.ks1;
+    if (p.sh_half)
+        return 2 * (down ? p.n_rb2 : p.n_rb1) * ks;
+    return (down ? p.n_rb2 : p.n_rb1 / p.span1) * ks;
+}
+
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -278,12 +290,13 @@ __device__ void bucket_block(const Params &p, int m)
     }
     if (tid == 0) {
         p.offsets[E] = total;
-        const int n1 = (ngroups + ngs) * (p.n_rb1 / p.span1) * p.ks1;
+        const int n1 = ngs * shared_items(p, false) + ngroups * (p.n_rb1 / p.span1) * p.ks1;
         P->m = m;
         P->n_hit = nhit;
         P->n_groups = ngroups + ngs;
+        P->n_sgroups = ngs;
         P->n_items1 = n1;
-        P->n_items = n1 + (ngroups + ngs) * p.n_rb2 * p.ks2;
+        P->n_items = n1 + ngs * shared_items(p, true) + ngroups * p.n_rb2 * p.ks2;
         for (int i = 0; i < kDoneSlots; ++i)
             p.ctr->items_done[i] = 0;
         p.ctr->error_word = 0;
@@ -689,6 +702,7 @@ __device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLAS
 // rows for down).
 struct Item {
     int valid, down, e, off, R, u, rb, kq, span;
+    int half;  // -1: whole row blocks; 0 / 1: that half of row block rb only
 };
 
 // Row-group table of the plan, cached in LDS by every block: expert, first
@@ -697,23 +711,41 @@ struct GroupLds {
     int expert[kMaxGroups], off[kMaxGroups], rows[kMaxGroups];
 };
 
-__device__ __forceinline__ Item make_item(const Params &p, int n_items, int n_items1,
+// Ticket t of a phase (gate/up, then down) maps to a row group, a row block
+// and a column split; the shared expert's groups come first. Where its items
+// cover half row blocks (6-bit codes), a row block has two halves per split.
+__device__ __forceinline__ Item make_item(const Params &p, int n_items, int n_items1, int n_sg,
                                           const GroupLds &gl, int ticket)
 {
     Item it{};
     it.valid = ticket < n_items;
+    it.half = -1;
     if (!it.valid)
         return it;
     it.down = ticket >= n_items1;
-    const int t = it.down ? ticket - n_items1 : ticket;
+    int t = it.down ? ticket - n_items1 : ticket;
     const int ks = it.down ? p.ks2 : p.ks1;
-    it.span = it.down ? 1 : p.span1;
-    const int per_u = (it.down ? p.n_rb2 : p.n_rb1 / p.span1) * ks;
-    it.u = t / per_u;
-    const int rem = t - it.u * per_u;
-    const int rbs = rem / ks;
-    it.rb = rbs * it.span;
-    it.kq = rem - rbs * ks;
+    const int per_s = shared_items(p, it.down);
+    if (t < n_sg * per_s) {
+        it.u = t / per_s;
+        const int rem = t - it.u * per_s;
+        const int rbh = rem / ks;  // row block (or half row block) index
+        it.kq = rem - rbh * ks;
+        it.span = p.sh_half ? 1 : (it.down ? 1 : p.span1);
+        it.rb = p.sh_half ? rbh >> 1 : rbh * it.span;
+        if (p.sh_half)
+            it.half = rbh & 1;
+    } else {
+        t -= n_sg * per_s;
+        it.span = it.down ? 1 : p.span1;
+        const int per_u = (it.down ? p.n_rb2 : p.n_rb1 / p.span1) * ks;
+        const int v = t / per_u;
+        const int rem = t - v * per_u;
+        const int rbs = rem / ks;
+        it.u = n_sg + v;
+        it.rb = rbs * it.span;
+        it.kq = rem - rbs * ks;
+    }
     it.e = uniform(gl.expert[it.u]);
     it.off = uniform(gl.off[it.u]);
     it.R = uniform(gl.rows[it.u]);
@@ -762,8 +794,11 @@ __device__ __forceinline__ WaveJob make_job(const Params &p, const DescRaw &d, c
     J.G = it.down ? p.I / 128 : p.H / 128;
     // a 6-bit wave takes kWaveRB / 2 tiles per row block unit (see load_group)
     const int per_wave = has6<CLASS> && J.bits == 6 ? kWaveRB / 2 : kWaveRB;
-    J.rb0 = it.down ? it.rb * 16 + wave * per_wave
-                    : it.rb * 8 + (wave % (kExpertWaves / 2)) * per_wave;
+    // a half-row-block item starts at its half (16-row tiles: 8 per gate/up
+    // row block, 16 per down row block)
+    const int hoff = it.half > 0 ? (it.down ? 8 : 4) : 0;
+    J.rb0 = it.down ? it.rb * 16 + hoff + wave * per_wave
+                    : it.rb * 8 + hoff + (wave % (kExpertWaves / 2)) * per_wave;
     J.g0 = it.kq * NG;
     return J;
 }
@@ -948,9 +983,11 @@ __device__ __forceinline__ void complete_item(const Params &p, const Item &it, S
         return;
     wait_stores();
     __syncthreads();
+    // a row block's arrivals: one per column split, or two (one per half)
+    const uint32_t arrivals = (uint32_t)(p.ks1 << (it.half >= 0 ? 1 : 0));
     if (tid < it.span)
         sm.last[tid] = atomic_add_agent(&p.rb_done[(it.u * p.n_rb1 + it.rb + tid) * kCtrStride],
-                                        1u) == (uint32_t)(p.ks1 - 1);
+                                        1u) == arrivals - 1u;
     __syncthreads();
     int finished = 0;
     for (int s = 0; s < it.span; ++s)
@@ -1011,7 +1048,7 @@ void expert_kernel(Params p)
     // 6-bit codebook slot: the waves of one gate/up half (same tensor in every item)
     const uint32_t lut_slot = (uint32_t)(wave / (kExpertWaves / kLut6Slots));
     const int m = uniform(P->m), n_items = uniform(P->n_items), n_items1 = uniform(P->n_items1);
-    const int n_groups = uniform(P->n_groups);
+    const int n_groups = uniform(P->n_groups), n_sg = uniform(P->n_sgroups);
 
     // token of each bucket row: routed rows from the row list, then the
     // shared expert's row m*k + t of token t
@@ -1025,7 +1062,7 @@ void expert_kernel(Params p)
     __syncthreads();
 
     int ticket = blockIdx.x;
-    Item cur = make_item(p, n_items, n_items1, s_grp, ticket);
+    Item cur = make_item(p, n_items, n_items1, n_sg, s_grp, ticket);
     uint32_t done = 0;
     if (cur.valid) {
         GroupBuf<CLASS> bA, bB;
@@ -1036,12 +1073,12 @@ void expert_kernel(Params p)
         while (true) {
             // 6-bit items: each row block takes two units of half the rows
             const int six = (has6<CLASS> && J.bits == 6) ? 1 : 0;
-            const bool last = sb + 1 == (cur.span << six);
+            const bool last = sb + 1 == (cur.half >= 0 ? 1 : cur.span << six);
             const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
             // after the item's last row block comes the next item: its plan
             // entries (LDS) and descriptor (vector loads)
             const int nxt_ticket = ticket + (int)gridDim.x;
-            const Item nxt = make_item(p, n_items, n_items1, s_grp, last ? nxt_ticket : n_items);
+            const Item nxt = make_item(p, n_items, n_items1, n_sg, s_grp, last ? nxt_ticket : n_items);
             const DescRaw dn = load_desc(p, nxt, wave);
 
             bool ok = true;

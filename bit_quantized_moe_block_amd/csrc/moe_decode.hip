@@ -172,6 +172,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
         p.has6 |= cfg->tensors[i].bits == 6;
     for (int i = 0; cfg->shared && i < 3; ++i)
         p.has6 |= cfg->shared[i].bits == 6;
+    p.sh_half = cfg->shared && cfg->shared[0].bits == 6;
     p.pair_cap = p.max_tokens * (p.k + p.has_shared);
     p.spin_limit = 2u * 1000u * 1000u;  // polls of up to ~1 us: a ~2 s bound
     p.signs_h = cfg->signs_hidden;

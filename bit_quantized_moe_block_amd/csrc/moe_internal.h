@@ -44,7 +44,8 @@ struct Plan {
     int32_t n_groups;      // row groups (<= 16 rows each)
     int32_t n_items1;      // gate/up work items
     int32_t n_items;       // all work items
-    int32_t pad[3];
+    int32_t n_sgroups;     // row groups of the shared expert (groups 0 .. n_sgroups-1)
+    int32_t pad[2];
     int32_t g_expert[kMaxGroups];  // expert of group u (groups in expert order)
     int32_t g_off[kMaxGroups];     // first row of u in the bucket row list
     int32_t g_rows[kMaxGroups];    // rows of u (1..16)
@@ -73,6 +74,8 @@ struct Params {
     int32_t has6;          // 1: some tensor has 6-bit codes (selects the kernel with that path)
     int32_t has_shared;    // 1: an always-on shared expert (tensors 3E..3E+2, bucket
                            // rows m*k + t, group expert id E)
+    int32_t sh_half;       // 1: the shared expert's items cover half row blocks (its
+                           // 6-bit codes make a full row block three 2-bit ones)
     uint32_t spin_limit;   // polls before a dependency wait gives up
     float *out;            // [m][H] result of the current launch
     const DevTensor *tensors;   // [E*3 + 3] (the last three: the shared expert)
