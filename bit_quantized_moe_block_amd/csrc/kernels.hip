@@ -1083,18 +1083,10 @@ void expert_kernel(Params p)
 
             bool ok = true;
             if (sb == 0) {
-                // the item's activation rows (a down item's rows once its h is
-                // complete, bounded wait), then its codebook and first weight
-                // group; only the rows are waited on before the LDS commit,
-                // and the second group follows it
-                if (cur.down) {
-                    if (tid == 0)
-                        sm.flag = wait_h(p, cur.u);
-                    __syncthreads();
-                    ok = sm.flag != 0;
-                }
-                St st;
-                st.issue(p, cur, s_tok);
+                // the item's codebook and first two weight groups, then (down
+                // items: once thread 0 has seen the group's h complete, a
+                // bounded wait) its activation rows: the weights do not
+                // depend on h and load during the wait
                 u32x4 lut = u32x4{0, 0, 0, 0};
                 _Float16 lut6 = 0;
                 if constexpr (is_cb<CLASS>) {
@@ -1103,12 +1095,19 @@ void expert_kernel(Params p)
                         lut6 = J.lut6(lane);
                 }
                 load_group<CLASS, 0>(bA, J, 0, lane, sc_lane);
-                st.commit(cur, Abuf);
                 if constexpr (NG > 1)
                     load_group<CLASS, 0>(bB, J, 1, lane, sc_lane);
+                if (cur.down) {
+                    if (tid == 0)
+                        sm.flag = wait_h(p, cur.u);
+                    __syncthreads();
+                    ok = sm.flag != 0;
+                }
+                St st;
+                st.issue(p, cur, s_tok);
+                st.commit(cur, Abuf);
                 // a 6-bit codebook goes to the wave pair's LDS slot (the waves
-                // sharing it write the same values), after the group loads so
-                // that waiting for it does not wait for them
+                // sharing it write the same values)
                 if (has6<CLASS> && J.bits == 6)
                     s_lut6[lut_slot * 64 + lane] = lut6;
                 __syncthreads();
