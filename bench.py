@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack43",
                     choices=["stack43", "pack46", "stack43_shared", "shared_layer", "full_layer",
-                             "rank_share", "nvfp4", "tiny"])
+                             "prefill", "rank_share", "nvfp4", "tiny"])
     ap.add_argument("--m", type=int, default=None, help="tokens per step (default: workload's)")
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the stack (default: the workload's, 43 for stack43)")
@@ -261,33 +261,42 @@ def main():
         f"({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     # ---- CPU oracle on a bounded sample: whole layers of the same workload
-    # (all m tokens each) until about 10 s of CPU work, at most 4 layers
+    # (all m tokens each, or the first 16 tokens when m > 24) until about
+    # 10 s of CPU work, at most 4 layers
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         cpu_s, cpu_bytes, rel, threads, done_layers = 0.0, 0.0, 0.0, 0, 0
+        tok = None if m <= 24 else list(range(16))
         for li in range(min(4, n_layers)):
             rid, _ = oracle.route(gen.make_logits(w, li, m), w.top_k)
-            d = gen.make_layer(w, li, experts=np.unique(rid))
+            used = np.unique(rid if tok is None else rid[tok])
+            d = gen.make_layer(w, li, experts=used)
             d["workload"] = w
             case = dict(d, m=m, x=gen.make_x(w, li, m), logits=gen.make_logits(w, li, m))
             L = oracle.Layer.from_case(case)
             t = time.perf_counter()
-            r = L.run(case["x"], case["logits"])
+            r = L.run(case["x"], case["logits"], tokens=tok)
             cpu_s += time.perf_counter() - t
-            cpu_bytes += weight_bytes[li]
+            if tok is None:
+                cpu_bytes += weight_bytes[li]
+            else:
+                ex = np.append(used, layers[li].E) if layers[li].has_shared else used
+                cpu_bytes += layers[li].weight_bytes(ex)
             threads = int(r["threads"])
             done_layers += 1
-            ref = r["out"]
-            got = inputs[li][2].cpu().numpy().astype(np.float64)
+            rows = slice(None) if tok is None else tok
+            ref = r["out"][rows]
+            got = inputs[li][2].cpu().numpy().astype(np.float64)[rows]
             rel = max(rel, float(np.max(np.max(np.abs(got - ref), 1) / np.max(np.abs(ref), 1))))
             del L, case, d
             if cpu_s >= 10.0:
                 break
         cpu = {"value": cpu_bytes / cpu_s / 1e9, "unit": "GB/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{done_layers} whole layer(s) of {w.name} (layers 0..{done_layers - 1}, "
-                         f"all {m} tokens, hit experts only), {cpu_s:.1f} s of CPU time",
+               "sample": f"{done_layers} layer(s) of {w.name} (layers 0..{done_layers - 1}, "
+                         + (f"all {m} tokens" if tok is None else f"tokens 0..15 of {m}")
+                         + f", hit experts only), {cpu_s:.1f} s of CPU time",
                "rel_err_vs_gpu": rel}
         log(f"oracle {cpu_s:.1f} s on {threads} threads over {done_layers} layer(s) -> "
             f"{cpu['value']:.4f} GB/s; GPU vs oracle rel {rel:.2e}")

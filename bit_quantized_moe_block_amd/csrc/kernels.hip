@@ -230,36 +230,48 @@ __device__ void route_token(const Params &p, const float *__restrict__ logits, i
     }
 }
 
+// Dynamic LDS of the route kernel: the bucketing block's per-expert token
+// bitmasks and row bases, W = ceil(m / 32) words per expert each.
+size_t route_lds_bytes(int E, int m)
+{
+    return (size_t)2 * E * ((m + 31) / 32) * sizeof(uint32_t);
+}
+
 // The last top-k block to finish builds the buckets: per-expert rows, row
 // groups (<= 16 rows each), the work plan, and clears the expert kernel's
 // counters (every run and every graph replay starts clean without a memset).
 __device__ void bucket_block(const Params &p, int m)
 {
-    __shared__ uint32_t s_mask[kMaxExperts];
-    __shared__ int s_off[kMaxExperts];
+    extern __shared__ uint32_t s_route[];  // [E][W] token masks, then [E][W] row bases
     __shared__ int tmp[kRouteWaves];
     const int tid = threadIdx.x;
-    const int E = p.E, k = p.k;
-    for (int e = tid; e < kMaxExperts; e += kRouteThreads)
-        s_mask[e] = 0u;
+    const int E = p.E, k = p.k, W = (m + 31) >> 5;
+    uint32_t *s_mask = s_route;
+    int *s_base = (int *)(s_route + E * W);
+    for (int i = tid; i < E * W; i += kRouteThreads)
+        s_mask[i] = 0u;
     __syncthreads();
 
     // ---- buckets. Top-k picks distinct experts per token, so expert e's rows
-    // are the tokens of the bitmask mask[e] (t < m <= 32), ascending by t;
-    // the rank of (t, j) inside e's bucket is popcount(mask[e] below bit t).
+    // are the tokens of its bitmask (bit t % 32 of word t / 32), ascending by
+    // t; the rank of (t, j) inside e's bucket is the count of mask bits below t.
     const int np = m * k;
-    for (int i = tid; i < np; i += kRouteThreads)
-        atomicOr(&s_mask[ld_coherent_i32(&p.ids[i])], 1u << (i / k));
+    for (int i = tid; i < np; i += kRouteThreads) {
+        const int t = i / k;
+        atomicOr(&s_mask[ld_coherent_i32(&p.ids[i]) * W + (t >> 5)], 1u << (t & 31));
+    }
     __syncthreads();
-    const uint32_t mask = tid < E ? s_mask[tid] : 0u;
-    const int cnt = __popc(mask);
+    int cnt = 0;
+    if (tid < E)
+        for (int w = 0; w < W; ++w)
+            cnt += __popc(s_mask[tid * W + w]);
     const int ng_e = (cnt + kGroupRows - 1) / kGroupRows;
-    // one scan of (rows | hit << 12 | groups << 22): sums stay below 4096 / 1024 / 1024
+    const int nhit = __syncthreads_count(cnt > 0);
+    // one scan of (rows | groups << 16): rows <= 8192, groups <= 768
     int packed_total;
-    const int packed = block_excl_scan(cnt | ((cnt > 0) << 12) | (ng_e << 22), tmp, packed_total);
-    const int off = packed & 0xFFF, gbase = packed >> 22;
-    const int total = packed_total & 0xFFF, nhit = (packed_total >> 12) & 0x3FF,
-              ngroups = packed_total >> 22;
+    const int packed = block_excl_scan(cnt | (ng_e << 16), tmp, packed_total);
+    const int off = packed & 0xFFFF, gbase = packed >> 16;
+    const int total = packed_total & 0xFFFF, ngroups = packed_total >> 16;
     Plan *P = p.plan;
     // the shared expert (if any) comes first: expert id E, bucket rows
     // m*k + t for every token t, in row groups of <= 16. It is the largest
@@ -272,7 +284,11 @@ __device__ void bucket_block(const Params &p, int m)
         P->g_rows[tid] = min(kGroupRows, m - kGroupRows * tid);
     }
     if (tid < E) {
-        s_off[tid] = off;
+        int base = off;
+        for (int w = 0; w < W; ++w) {
+            s_base[tid * W + w] = base;
+            base += __popc(s_mask[tid * W + w]);
+        }
         p.counts[tid] = cnt;
         p.offsets[tid] = off;
         for (int g = 0; g < ng_e; ++g) {
@@ -284,7 +300,7 @@ __device__ void bucket_block(const Params &p, int m)
     __syncthreads();
     for (int i = tid; i < np; i += kRouteThreads) {
         const int e = ld_coherent_i32(&p.ids[i]), t = i / k;
-        const int q = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
+        const int q = s_base[e * W + (t >> 5)] + __popc(s_mask[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
         p.rows[q] = i;
         p.pos[i] = q;
     }
@@ -705,10 +721,11 @@ struct Item {
     int half;  // -1: whole row blocks; 0 / 1: that half of row block rb only
 };
 
-// Row-group table of the plan, cached in LDS by every block: expert, first
-// bucket row and rows of group u.
+// Row-group table of the plan, cached in LDS by every block (in the dynamic
+// LDS, after the staged rows, p.gcap entries each): expert, first bucket row
+// and rows of group u.
 struct GroupLds {
-    int expert[kMaxGroups], off[kMaxGroups], rows[kMaxGroups];
+    const int *expert, *off, *rows;
 };
 
 // Ticket t of a phase (gate/up, then down) maps to a row group, a row block
@@ -775,6 +792,17 @@ __device__ __forceinline__ DescRaw load_desc(const Params &p, const Item &it, in
     d.d0 = __builtin_amdgcn_raw_buffer_load_b128(r, 0, idx * (int)sizeof(DevTensor), 0);
     d.d1 = __builtin_amdgcn_raw_buffer_load_b128(r, 16, idx * (int)sizeof(DevTensor), 0);
     return d;
+}
+
+// Token of bucket row min(r16, R-1) of a gate/up item's group, for lane r16:
+// routed rows from the row list, the shared expert's row m*k + t is token t.
+// Loaded one item ahead, with the item's descriptor.
+__device__ __forceinline__ int load_token(const Params &p, const Item &it, int m, int r16)
+{
+    if (!it.valid || it.down)
+        return 0;
+    const int q = it.off + min(r16, it.R - 1);
+    return q < m * p.k ? p.rows[q] / p.k : q - m * p.k;
 }
 
 // The matrix part wave `wave` computes for item `it`: a gate/up item's 128
@@ -905,7 +933,7 @@ struct Stage {
     static constexpr int ASTRIDE = KC + kLdsPadHalves;   // LDS row stride (halves)
     u32x4 v[ITERS];
 
-    __device__ __forceinline__ void issue(const Params &p, const Item &it, const int *s_tok)
+    __device__ __forceinline__ void issue(const Params &p, const Item &it, int tok)
     {
         const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
         const int wave_first = uniform(tid & ~63);
@@ -922,7 +950,8 @@ struct Stage {
                 const _Float16 *base = p.hr + (size_t)it.off * p.I + col0;
                 v[k] = ld_coherent16(base, (uint32_t)((r * p.I + cc) * 2));
             } else {
-                const _Float16 *row = p.xr + (size_t)s_tok[it.off + r] * p.H + col0;
+                // token of row r: lane r of the wave holds it (see load_token)
+                const _Float16 *row = p.xr + (size_t)__shfl(tok, r) * p.H + col0;
                 v[k] = *(const u32x4 GLOBAL *)(row + cc);
             }
         }
@@ -1036,10 +1065,8 @@ template <int CLASS, int NG>
 __global__ __launch_bounds__(kExpertThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void expert_kernel(Params p)
 {
-    extern __shared__ _Float16 Abuf[];  // min(m, 16) staged rows
+    extern __shared__ _Float16 Abuf[];  // min(m, 16) staged rows, then the row-group table
     __shared__ Smem sm;
-    __shared__ int s_tok[kMaxPairs];    // token of each bucket row
-    __shared__ GroupLds s_grp;
     using St = Stage<NG>;
     const Plan *P = p.plan;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1050,19 +1077,18 @@ void expert_kernel(Params p)
     const int m = uniform(P->m), n_items = uniform(P->n_items), n_items1 = uniform(P->n_items1);
     const int n_groups = uniform(P->n_groups), n_sg = uniform(P->n_sgroups);
 
-    // token of each bucket row: routed rows from the row list, then the
-    // shared expert's row m*k + t of token t
-    for (int i = tid; i < m * (p.k + p.has_shared); i += kExpertThreads)
-        s_tok[i] = i < m * p.k ? p.rows[i] / p.k : i - m * p.k;
+    int *s_tab = (int *)((char *)Abuf + p.lds_tab);
+    const GroupLds s_grp{s_tab, s_tab + p.gcap, s_tab + 2 * p.gcap};
     for (int i = tid; i < n_groups; i += kExpertThreads) {
-        s_grp.expert[i] = P->g_expert[i];
-        s_grp.off[i] = P->g_off[i];
-        s_grp.rows[i] = P->g_rows[i];
+        s_tab[i] = P->g_expert[i];
+        s_tab[p.gcap + i] = P->g_off[i];
+        s_tab[2 * p.gcap + i] = P->g_rows[i];
     }
     __syncthreads();
 
     int ticket = blockIdx.x;
     Item cur = make_item(p, n_items, n_items1, n_sg, s_grp, ticket);
+    int tok = load_token(p, cur, m, r16);
     uint32_t done = 0;
     if (cur.valid) {
         GroupBuf<CLASS> bA, bB;
@@ -1080,6 +1106,7 @@ void expert_kernel(Params p)
             const int nxt_ticket = ticket + (int)gridDim.x;
             const Item nxt = make_item(p, n_items, n_items1, n_sg, s_grp, last ? nxt_ticket : n_items);
             const DescRaw dn = load_desc(p, nxt, wave);
+            const int tok_n = load_token(p, nxt, m, r16);
 
             bool ok = true;
             if (sb == 0) {
@@ -1104,7 +1131,7 @@ void expert_kernel(Params p)
                     ok = sm.flag != 0;
                 }
                 St st;
-                st.issue(p, cur, s_tok);
+                st.issue(p, cur, tok);
                 st.commit(cur, Abuf);
                 // a 6-bit codebook goes to the wave pair's LDS slot (the waves
                 // sharing it write the same values)
@@ -1151,6 +1178,7 @@ void expert_kernel(Params p)
                 break;
             ticket = nxt_ticket;
             cur = nxt;
+            tok = tok_n;
             sb = 0;
             J = make_job<CLASS, NG>(p, dn, nxt, wave);
         }
@@ -1232,7 +1260,7 @@ hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits,
 {
     const int tasks = m * (p.H / 128);
     const int blocks = (m + kRouteWaves - 1) / kRouteWaves + (tasks + kRouteWaves - 1) / kRouteWaves;
-    route_kernel<<<dim3(blocks), dim3(kRouteThreads), 0, s>>>(p, x, logits, m);
+    route_kernel<<<dim3(blocks), dim3(kRouteThreads), route_lds_bytes(p.E, m), s>>>(p, x, logits, m);
     return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@ struct moe_decode_s {
     std::vector<int> bpc;        // [m] resident blocks per CU
     std::vector<size_t> lds;     // [m] dynamic LDS bytes
     std::vector<int> span1;      // [m] 128-row blocks per gate/up item
+    std::vector<int> gcap;       // [m] row-group table entries (bound on the groups)
+    std::vector<int> lds_tab;    // [m] byte offset of the group table in the dynamic LDS
     bool bound = false;
     hipStream_t stream = nullptr;
     bool ran = false;
@@ -73,6 +75,16 @@ static int split_cols(int H, int I)
         if ((H / 128) % d == 0 && (I / 128) % d == 0)
             best = d;
     return 128 * best;
+}
+
+// Upper bound on the row groups of a run with m tokens: an expert with R
+// rows has ceil(R / 16) <= R / 16 + 1 groups, at most min(E, m k) experts
+// are hit, and the shared expert adds ceil(m / 16).
+static int group_cap(const Params &p, int m)
+{
+    const int np = m * p.k;
+    return std::min(p.E, np) + (np + kGroupRows - 1) / kGroupRows +
+           (p.has_shared ? (m + kGroupRows - 1) / kGroupRows : 0);
 }
 
 static moe_status validate(const moe_decode_config *c)
@@ -207,8 +219,9 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
                  o_offsets = take(4 * (E + 1)), o_rows = take(4 * PC), o_pos = take(4 * PC);
     const size_t o_plan = take(sizeof(Plan));
     const size_t ctr_b = 4 * kCtrStride;  // one counter per 128-byte line
-    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(ctr_b * kMaxGroups * p.n_rb1),
-                 o_hready = take(ctr_b * kMaxGroups);
+    const size_t gmax = group_cap(p, p.max_tokens);
+    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(ctr_b * gmax * p.n_rb1),
+                 o_hready = take(ctr_b * gmax);
     const size_t ctr_end = off;
     const size_t o_xr = take(2 * M * H), o_gu = take(4 * (size_t)p.ks1 * PC * 2 * I),
                  o_hr = take(2 * PC * I), o_y = take(4 * (size_t)p.ks2 * PC * H);
@@ -259,9 +272,17 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     h->bpc.assign(M + 1, 0);
     h->lds.assign(M + 1, 0);
     h->span1.assign(M + 1, 1);
+    h->gcap.assign(M + 1, 0);
+    h->lds_tab.assign(M + 1, 0);
     for (int m = 1; m <= (int)M; ++m) {
         h->span1[m] = (m >= 8 && p.n_rb1 % 2 == 0) ? 2 : 1;
-        const size_t lds = (size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) * sizeof(_Float16);
+        // dynamic LDS: the staged rows (min(m, 16) x kc halves, padded), then
+        // the row-group table (3 ints per group)
+        const size_t stage = ((size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) *
+                                  sizeof(_Float16) + 15) & ~size_t(15);
+        h->gcap[m] = group_cap(p, m);
+        h->lds_tab[m] = (int)stage;
+        const size_t lds = stage + 3 * sizeof(int) * (size_t)h->gcap[m];
         int bpc = 0;
         err = expert_occupancy(p.format, p.kc1 / 128, p.has6 != 0, &bpc, lds);
         if (err != hipSuccess || bpc < 1)
@@ -299,6 +320,8 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
     Params p = h->p;
     p.out = out;
     p.span1 = h->span1[m];
+    p.gcap = h->gcap[m];
+    p.lds_tab = h->lds_tab[m];
     HIP_TRY(launch_route(p, (const uint16_t *)x_bf16, logits, m, s));
     if (h->ev_begin)
         HIP_TRY(hipEventRecord(h->ev_begin, s));

@@ -9,7 +9,7 @@ namespace moe {
 constexpr int kThreads = 256;       // every kernel: 4 wave64s
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
-constexpr int kMaxTokens = 32;
+constexpr int kMaxTokens = 512;
 // Bucket rows: k routed rows per token, plus one per token for a shared expert.
 constexpr int kMaxPairs = kMaxTokens * (kMaxTopK + 1);
 constexpr int kGroupRows = 16;      // rows of one MFMA token block
@@ -76,6 +76,8 @@ struct Params {
                            // rows m*k + t, group expert id E)
     int32_t sh_half;       // 1: the shared expert's items cover half row blocks (its
                            // 6-bit codes make a full row block three 2-bit ones)
+    int32_t gcap;          // row-group table entries in LDS (bound on the groups of a run)
+    int32_t lds_tab;       // byte offset of that table in the expert kernel's dynamic LDS
     uint32_t spin_limit;   // polls before a dependency wait gives up
     float *out;            // [m][H] result of the current launch
     const DevTensor *tensors;   // [E*3 + 3] (the last three: the shared expert)
@@ -99,6 +101,7 @@ struct Params {
 };
 
 // Kernel launchers (kernels.hip).
+size_t route_lds_bytes(int E, int m);
 hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits, int m,
                         hipStream_t s);
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s);

@@ -103,7 +103,11 @@ typedef struct {
     int32_t top_k;                   /* k, 1..min(16, E) */
     int32_t hidden;                  /* H, multiple of 256, <= 16384 */
     int32_t inter;                   /* I, multiple of 128, <= 16384 */
-    int32_t max_tokens;              /* largest m passed to run(), 1..32 */
+    int32_t max_tokens;              /* largest m passed to run(), 1..512. Decode is m <= 24;
+                                        larger m (prefill, batched verify) run the same
+                                        kernels on more row groups. The scratch grows
+                                        linearly with max_tokens (about 0.9 MiB per token
+                                        at top-8, H = 4096, I = 2048) */
     const moe_tensor_desc *tensors;  /* host [E*3]: expert e -> gate, up, down at 3e, 3e+1, 3e+2;
                                         copied at create */
     const int8_t *signs_hidden;      /* device int8 [H] of +1/-1 (codebook; NULL for NVFP4) */

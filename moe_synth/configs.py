@@ -64,6 +64,10 @@ WORKLOADS = {
     # The 43-layer stack with the shared expert in every layer.
     "stack43_shared": Workload("stack43_shared", 8, 256, 8, 4096, 2048, "codebook", "mix62",
                                "zipf", (16,), layers=43, shared_bits=6),
+    # Prefill / batched verify: the full layer at 64..512 tokens (one batch of
+    # BT = 512 at most), four layers in one graph.
+    "prefill": Workload("prefill", 9, 256, 8, 4096, 2048, "codebook", "mix62", "zipf",
+                        (64, 128, 256, 512), layers=4),
     # NVFP4 experts (e2m1 values, e4m3 per-16 scales, fp32 tensor scale).
     "nvfp4": Workload("nvfp4", 5, 256, 8, 4096, 2048, "nvfp4", "nvfp4", "normal", (2, 8)),
 }

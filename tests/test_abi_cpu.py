@@ -75,7 +75,7 @@ def create_status(cfg):
     (dict(inter=100), B.MOE_E_INVALID, "inter"),
     (dict(hidden=32768), B.MOE_E_UNSUPPORTED, "16384"),
     (dict(max_tokens=0), B.MOE_E_INVALID, "max_tokens"),
-    (dict(max_tokens=33), B.MOE_E_UNSUPPORTED, "max_tokens"),
+    (dict(max_tokens=513), B.MOE_E_UNSUPPORTED, "max_tokens"),
     (dict(signs_hidden=None), B.MOE_E_INVALID, "signs"),
 ])
 def test_create_rejects_bad_config(over, status, msg):

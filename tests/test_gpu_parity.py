@@ -319,3 +319,44 @@ def test_nvfp4_full_sampled(m):
     d["workload"] = w
     case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
     parity(case, tokens=sorted(set([0, m - 1])), max_tokens=8)
+
+
+# Large m (prefill / batched verify, up to 512 tokens): the same kernels with
+# many row groups per expert. Zipf routing sends hundreds of rows to the hot
+# experts (tens of 16-row groups each).
+LARGE_M = [
+    (small_workload("lm1", 16, 4, 256, 128, bits_mix="alternate", router="zipf", config_id=401), 33),
+    (small_workload("lm2", 32, 8, 512, 256, bits_mix="all3", router="zipf", config_id=402), 100),
+    (small_workload("lm3", 64, 8, 512, 256, bits_mix="alternate", config_id=403), 257),
+    (small_workload("lm4", 16, 2, 256, 128, bits_mix="all2", router="zipf", config_id=404), 512),
+    (small_workload("lm5", 32, 4, 256, 128, bits_mix="alternate", config_id=405, shared_bits=6), 300),
+]
+
+
+@pytest.mark.parametrize("w,m", LARGE_M, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_large_m_small_shapes(w, m):
+    parity(gen.make_case(w, m))
+
+
+def test_prefill_layer_sampled_and_repeatable():
+    # The full 256-expert layer at m = 512: exact routing and buckets for all
+    # tokens, three tokens against the oracle, and a second run bit-identical.
+    w = WORKLOADS["prefill"]
+    m = 512
+    case = gen.make_case(w, m)
+    tokens = [0, 255, 511]
+    say(f"[parity] prefill m={m}")
+    dl = DeviceLayer.from_case(case, max_tokens=m)
+    try:
+        out = run_gpu(dl, case)
+        check_routing(dl, case, m)
+        st = dl.stats()
+        assert st.error_word == 0 and st.items_done == st.items
+        out2 = run_gpu(dl, case)
+        assert np.array_equal(out, out2)
+        ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+        err = rel_err(out, ref["out"], tokens)
+        say(f"    rel={err:.3e} hit={st.hit_experts} items={st.items}")
+        assert err <= REL_TOL
+    finally:
+        dl.close()
