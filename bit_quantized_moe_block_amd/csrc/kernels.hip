@@ -238,7 +238,7 @@ size_t route_lds_bytes(int E, int m)
 }
 
 // The last top-k block to finish builds the buckets: per-expert rows, row
-// groups (<= 16 rows each), the work plan, and clears the expert kernel's
+// groups (<= p.group_rows rows each), the work plan, and clears the expert kernel's
 // counters (every run and every graph replay starts clean without a memset).
 __device__ void bucket_block(const Params &p, int m)
 {
@@ -265,7 +265,8 @@ __device__ void bucket_block(const Params &p, int m)
     if (tid < E)
         for (int w = 0; w < W; ++w)
             cnt += __popc(s_mask[tid * W + w]);
-    const int ng_e = (cnt + kGroupRows - 1) / kGroupRows;
+    const int GR = p.group_rows;  // rows per row group: 16 (decode) or 64 (prefill)
+    const int ng_e = (cnt + GR - 1) / GR;
     const int nhit = __syncthreads_count(cnt > 0);
     // one scan of (rows | groups << 16): rows <= 8192, groups <= 768
     int packed_total;
@@ -274,14 +275,14 @@ __device__ void bucket_block(const Params &p, int m)
     const int total = packed_total & 0xFFFF, ngroups = packed_total >> 16;
     Plan *P = p.plan;
     // the shared expert (if any) comes first: expert id E, bucket rows
-    // m*k + t for every token t, in row groups of <= 16. It is the largest
+    // m*k + t for every token t, in row groups of <= GR. It is the largest
     // expert of the layer (every token, wider codes), so its items start
     // first and its down items are not the last to find their h.
-    const int ngs = p.has_shared ? (m + kGroupRows - 1) / kGroupRows : 0;
+    const int ngs = p.has_shared ? (m + GR - 1) / GR : 0;
     if (tid < ngs) {
         P->g_expert[tid] = E;
-        P->g_off[tid] = m * k + kGroupRows * tid;
-        P->g_rows[tid] = min(kGroupRows, m - kGroupRows * tid);
+        P->g_off[tid] = m * k + GR * tid;
+        P->g_rows[tid] = min(GR, m - GR * tid);
     }
     if (tid < E) {
         int base = off;
@@ -293,8 +294,8 @@ __device__ void bucket_block(const Params &p, int m)
         p.offsets[tid] = off;
         for (int g = 0; g < ng_e; ++g) {
             P->g_expert[ngs + gbase + g] = tid;
-            P->g_off[ngs + gbase + g] = off + kGroupRows * g;
-            P->g_rows[ngs + gbase + g] = min(kGroupRows, cnt - kGroupRows * g);
+            P->g_off[ngs + gbase + g] = off + GR * g;
+            P->g_rows[ngs + gbase + g] = min(GR, cnt - GR * g);
         }
     }
     __syncthreads();
@@ -487,10 +488,10 @@ struct WaveJob {
 // One register buffer of weight data: one 128-column group of the wave's
 // kWaveRB row blocks (tiles), with the lane's scales of each tile: the fp16
 // group scale (codebook) or the two e4m3 block scales (NVFP4).
-template <int CLASS>
+template <int CLASS, int NT = kWaveRB>
 struct GroupBuf {
-    uint32_t w[kWaveRB][Slot<CLASS>::W];
-    uint32_t sc[kWaveRB];
+    uint32_t w[NT][Slot<CLASS>::W];
+    uint32_t sc[NT];
 };
 
 // A wave-uniform value the compiler cannot prove uniform (it flows through
@@ -510,7 +511,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void GLOBAL 
     return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)b, 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Load group j (absolute group g0 + j) of job J into b. KB: codebook bits
+// Load group j (absolute group g0 + j) of job J into b (NT tiles). KB: codebook bits
 // when known at compile time, 0 to read them from the job. Buffer loads with
 // the tile offset in a scalar register and one per-lane offset, so a load in
 // flight holds no address registers; one VMEM instruction per tile whatever
@@ -521,8 +522,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void GLOBAL 
 // load exactly like a 3-bit slot (lane offset 12 bytes, the half in the
 // scalar offset) into buffer rows 2r (columns 0..15) and 2r + 1 (16..31):
 // same buffer shape, same count of loads, no extra address registers.
-template <int CLASS, int KB>
-__device__ __forceinline__ void load_group(GroupBuf<CLASS> &b, const WaveJob &J, int j, int lane,
+template <int CLASS, int KB, int NT = kWaveRB>
+__device__ __forceinline__ void load_group(GroupBuf<CLASS, NT> &b, const WaveJob &J, int j, int lane,
                                            int sc_lane)
 {
     const __amdgpu_buffer_rsrc_t rc = tensor_rsrc(J.codes);
@@ -530,7 +531,7 @@ __device__ __forceinline__ void load_group(GroupBuf<CLASS> &b, const WaveJob &J,
     const bool six = has6<CLASS> && J.bits == 6;
     const int g = J.g0 + j;
 #pragma unroll
-    for (int i = 0; i < kWaveRB; ++i) {
+    for (int i = 0; i < NT; ++i) {
         const int trow = six ? J.rb0 + (i >> 1) : J.rb0 + i;  // tile row block
         const int tile = trow * J.G + g;
         if constexpr (is_cb<CLASS>) {
@@ -1252,6 +1253,262 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Prefill / batched verify (more than 32 tokens): grouped GEMM over buckets
+// ---------------------------------------------------------------------------
+// With many tokens an expert has tens to hundreds of rows. The buckets are
+// cut into row groups of up to 64 rows, and each decoded weight step feeds the
+// MFMAs of all four 16-row subtiles of the group: the decode, the VALU cost
+// of these formats, is paid once per 64 rows instead of once per 16. A block
+// covers one row group and 128 output rows (of gate and of up: four waves
+// each) or 256 (down), over all input columns, so there are no column splits
+// and no partial sums. The gate/up block finishes SiLU(g) u and the h
+// rotation of its 128 rows itself (exactly one rotation block); the down
+// block writes y; the combine kernel sums the slots. The down kernel runs
+// after the gate/up kernel in stream order.
+
+constexpr int kPfThreads = 512;                   // 8 waves: 4 per projection (gate/up)
+constexpr int kPfWaves = kPfThreads / 64;
+constexpr int kPfNT = 2;                          // 16-row tiles per wave
+constexpr int kPfRows = 64;                       // rows of a prefill row group
+constexpr int kPfSub = kPfRows / 16;              // MFMA subtiles per row group
+constexpr int kPfAStride = 128 + kLdsPadHalves;   // staged chunk row stride (halves)
+constexpr int kPfHStride = 128 + 4;               // epilogue buffer row stride (floats)
+constexpr size_t kPfLds = 2 * kPfRows * kPfAStride * sizeof(_Float16);
+
+// One 128-column chunk of the group's activation rows: 64 rows x 128 fp16 =
+// 1024 16-byte pieces, two per thread; rows past R repeat row R-1 (their
+// results are never stored). Gate/up rows are tokens: lane r of every wave
+// holds the token of row r. Down rows off .. off+R-1 of h~ are consecutive.
+struct PfStage {
+    u32x4 v[2];
+    __device__ __forceinline__ void issue(const Params &p, bool down, int off, int R, int tok, int c)
+    {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = tid + k * kPfThreads;
+            const int row = min(i >> 4, R - 1), col = c * 128 + (i & 15) * 8;
+            const _Float16 *src = down ? p.hr + (size_t)(off + row) * p.I + col
+                                       : p.xr + (size_t)__shfl(tok, row) * p.H + col;
+            v[k] = *(const u32x4 GLOBAL *)src;
+        }
+    }
+    __device__ __forceinline__ void commit(_Float16 *A) const
+    {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = tid + k * kPfThreads;
+            *(u32x4 *)(A + (i >> 4) * kPfAStride + (i & 15) * 8) = v[k];
+        }
+    }
+};
+
+// One 128-column group of the wave's kPfNT tiles against the nsub staged
+// 16-row subtiles (A, B and result layouts as in process_group; subtile t =
+// rows 16t .. 16t+15). Per step: the subtiles' A operands, then per tile one
+// decode and nsub MFMAs. The group scale multiplies the decoded fp16 weights
+// (one more fp16 rounding, as the NVFP4 block scale), so the accumulators
+// take the products directly: per-group partial results for every (tile,
+// subtile) would not fit in the registers.
+template <int CLASS, int FMT>
+__device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const _Float16 *A,
+                                         int nsub, const uint32_t (&tab)[4],
+                                         floatx4 (&acc)[kPfNT][kPfSub])
+{
+    const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        half8 a[kPfSub];
+#pragma unroll
+        for (int t = 0; t < kPfSub; ++t)
+            a[t] = t < nsub ? *(const half8 *)(A + (16 * t + r16) * kPfAStride + q * 32 + s * 8)
+                            : half8{};
+#pragma unroll
+        for (int i = 0; i < kPfNT; ++i) {
+            half2v bs = half2v{1, 1};
+            if constexpr (FMT == 4) {
+                const _Float16 v = (_Float16)(s < 2 ? __builtin_amdgcn_cvt_f32_fp8(b.sc[i], 0)
+                                                    : __builtin_amdgcn_cvt_f32_fp8(b.sc[i], 1));
+                bs = half2v{v, v};
+            }
+            half8 bv = decode_step<FMT>(b.w[i], s, tab, bs);
+            if constexpr (FMT != 4) {
+                const _Float16 f = __builtin_bit_cast(_Float16, (uint16_t)b.sc[i]);
+                bv *= half8{f, f, f, f, f, f, f, f};
+            }
+#pragma unroll
+            for (int t = 0; t < kPfSub; ++t)
+                if (t < nsub)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
+        }
+    }
+}
+
+template <int CLASS>
+__device__ __forceinline__ void pf_group_any(const GroupBuf<CLASS, kPfNT> &b, int bits,
+                                             const _Float16 *A, int nsub, const uint32_t (&tab)[4],
+                                             floatx4 (&acc)[kPfNT][kPfSub])
+{
+    if constexpr (!is_cb<CLASS>)
+        pf_group<CLASS, 4>(b, A, nsub, tab, acc);
+    else if (bits == 3)
+        pf_group<CLASS, 3>(b, A, nsub, tab, acc);
+    else
+        pf_group<CLASS, 2>(b, A, nsub, tab, acc);
+}
+
+// Block b: row group u = b / RB, output row block rb = b % RB (RB = I / 128
+// gate/up blocks, H / 256 down blocks); blocks past the run's groups exit.
+// The chunks of the activations go through two LDS halves and the weight
+// groups through two register buffers: chunk c+1's activations and weight
+// group c+2 load while chunk c is computed.
+template <int CLASS, bool DOWN>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void prefill_kernel(Params p)
+{
+    extern __shared__ _Float16 pf_lds[];  // [2][64][kPfAStride]; the gate/up epilogue reuses it
+    const Plan *P = p.plan;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int RB = DOWN ? p.H / 256 : p.n_rb1;
+    const int u = blockIdx.x / RB, rb = blockIdx.x - u * RB;
+    if (u >= uniform(P->n_groups))
+        return;
+    const int e = uniform(P->g_expert[u]), off = uniform(P->g_off[u]), R = uniform(P->g_rows[u]);
+    const int m = uniform(P->m);
+    const int nsub = (R + 15) >> 4;
+    int tok = 0;  // gate/up: token of row `lane` of the group
+    if (!DOWN) {
+        const int qrow = off + min(lane, R - 1);
+        tok = qrow < m * p.k ? p.rows[qrow] / p.k : qrow - m * p.k;
+    }
+    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave >> 2)];
+    WaveJob J;
+    J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
+    J.scales = (gu8p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.scales);
+    J.lut = (const uint16_t *)(uintptr_t)uniform((uint64_t)(uintptr_t)d.lut);
+    J.ts = __uint_as_float((uint32_t)uniform((int)__float_as_uint(d.tensor_scale)));
+    J.bits = uniform(d.bits);
+    J.G = DOWN ? p.I / 128 : p.H / 128;
+    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 3) * kPfNT;
+    J.g0 = 0;
+    const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+
+    uint32_t tab[4] = {0, 0, 0, 0};
+    u32x4 lut = u32x4{0, 0, 0, 0};
+    if constexpr (is_cb<CLASS>)
+        lut = load_lut_raw(J);
+    // every load below is unconditional (a chunk index past the end reloads
+    // the last chunk): a load under a branch would merge with the buffer's
+    // old value, and the register copies that merge takes wait for every
+    // load in flight
+    GroupBuf<CLASS, kPfNT> bA, bB;
+    PfStage st;
+    const int G1 = J.G - 1;
+    st.issue(p, DOWN, off, R, tok, 0);
+    load_group<CLASS, 0, kPfNT>(bA, J, 0, lane, sc_lane);
+    st.commit(pf_lds);
+    load_group<CLASS, 0, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
+    __syncthreads();
+    if constexpr (is_cb<CLASS>)
+        lut_tables(lut, tab);
+
+    floatx4 acc[kPfNT][kPfSub];
+#pragma unroll
+    for (int i = 0; i < kPfNT; ++i)
+#pragma unroll
+        for (int t = 0; t < kPfSub; ++t)
+            acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    _Float16 *const half0 = pf_lds, *const half1 = pf_lds + kPfRows * kPfAStride;
+    // chunk c: weights from buffer c % 2 (refilled with chunk c + 2),
+    // activations from LDS half c % 2
+    auto step = [&](int c, GroupBuf<CLASS, kPfNT> &b) {
+        const _Float16 *A = (c & 1) ? half1 : half0;
+        _Float16 *Anext = (c & 1) ? half0 : half1;
+        st.issue(p, DOWN, off, R, tok, min(c + 1, G1));
+        if (c < J.G)
+            pf_group_any<CLASS>(b, J.bits, A, nsub, tab, acc);
+        load_group<CLASS, 0, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
+        st.commit(Anext);
+        __syncthreads();
+    };
+    for (int c = 0; c < J.G; c += 2) {
+        step(c, bA);
+        step(c + 1, bB);
+    }
+    if constexpr (!is_cb<CLASS>)
+#pragma unroll
+        for (int i = 0; i < kPfNT; ++i)
+#pragma unroll
+            for (int t = 0; t < kPfSub; ++t)
+                acc[i][t] *= J.ts;
+
+    // result layout: lane holds rows 16t + 4q + j (j = 0..3) of subtile t,
+    // output row 16i + r16 of the wave's tile i
+    if constexpr (DOWN) {
+        const int n0 = rb * 256 + wave * (kPfNT * 16);
+#pragma unroll
+        for (int i = 0; i < kPfNT; ++i)
+#pragma unroll
+            for (int t = 0; t < kPfSub; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 16 * t + 4 * q + j;
+                    if (t < nsub && row < R)
+                        p.y_part[(size_t)(off + row) * p.H + n0 + 16 * i + r16] = acc[i][t][j];
+                }
+    } else {
+        // h = silu(g) u through LDS (the up waves' u, then the gate waves'
+        // h in place), then each wave rotates the h of tokens wave, wave+4, ...
+        float *hb = (float *)pf_lds;  // [64 rows][kPfHStride]
+        const int lr0 = (wave & 3) * (kPfNT * 16);
+        if (wave >= 4)
+#pragma unroll
+            for (int i = 0; i < kPfNT; ++i)
+#pragma unroll
+                for (int t = 0; t < kPfSub; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = 16 * t + 4 * q + j;
+                        if (t < nsub && row < R)
+                            hb[row * kPfHStride + lr0 + 16 * i + r16] = acc[i][t][j];
+                    }
+        __syncthreads();
+        if (wave < 4)
+#pragma unroll
+            for (int i = 0; i < kPfNT; ++i)
+#pragma unroll
+                for (int t = 0; t < kPfSub; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = 16 * t + 4 * q + j;
+                        if (t < nsub && row < R) {
+                            float *hp = hb + row * kPfHStride + lr0 + 16 * i + r16;
+                            const float g = acc[i][t][j];
+                            *hp = g / (1.0f + expf(-g)) * *hp;
+                        }
+                    }
+        __syncthreads();
+        const int n = rb * 128 + 2 * lane;
+        for (int row = wave; row < R; row += kPfWaves) {
+            float v0 = hb[row * kPfHStride + 2 * lane], v1 = hb[row * kPfHStride + 2 * lane + 1];
+            if (p.format == kFmtCodebook) {
+                v0 *= (float)p.signs_i[n];
+                v1 *= (float)p.signs_i[n + 1];
+                wave_fwht128(v0, v1);
+                v0 *= kInvSqrt128;
+                v1 *= kInvSqrt128;
+            }
+            *(half2v *)(p.hr + (size_t)(off + row) * p.I + n) = half2v{(_Float16)v0, (_Float16)v1};
+        }
+    }
+    if (tid == 0)
+        atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], 1u);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -1296,6 +1553,22 @@ static void *expert_kernel_for(int format, int ng, bool six)
     case 2: return expert_fn<kFmtNvfp4, 2>();
     default: return expert_fn<kFmtNvfp4, 1>();
     }
+}
+
+// The two prefill kernels: grid_groups row groups (a bound on the run's
+// groups; blocks past them exit).
+hipError_t launch_prefill(const Params &p, int grid_groups, hipStream_t s)
+{
+    void *gu = p.format == kFmtCodebook ? (void *)prefill_kernel<kFmtCodebook, false>
+                                        : (void *)prefill_kernel<kFmtNvfp4, false>;
+    void *dn = p.format == kFmtCodebook ? (void *)prefill_kernel<kFmtCodebook, true>
+                                        : (void *)prefill_kernel<kFmtNvfp4, true>;
+    void *args[] = {const_cast<Params *>(&p)};
+    hipError_t err = hipLaunchKernel(gu, dim3(grid_groups * p.n_rb1), dim3(kPfThreads), args,
+                                     kPfLds, s);
+    if (err != hipSuccess)
+        return err;
+    return hipLaunchKernel(dn, dim3(grid_groups * (p.H / 256)), dim3(kPfThreads), args, kPfLds, s);
 }
 
 hipError_t launch_combine(const Params &p, int m, hipStream_t s)

@@ -34,11 +34,13 @@ struct moe_decode_s {
     std::vector<size_t> lds;     // [m] dynamic LDS bytes
     std::vector<int> span1;      // [m] 128-row blocks per gate/up item
     std::vector<int> gcap;       // [m] row-group table entries (bound on the groups)
+    std::vector<int> prefill;    // [m] 1: the prefill kernels (64-row groups) run this m
     std::vector<int> lds_tab;    // [m] byte offset of the group table in the dynamic LDS
     bool bound = false;
     hipStream_t stream = nullptr;
     bool ran = false;
     int last_m = 0;
+    bool last_prefill = false;
     hipEvent_t ev_begin = nullptr, ev_end = nullptr;
 };
 
@@ -80,12 +82,19 @@ static int split_cols(int H, int I)
 // Upper bound on the row groups of a run with m tokens: an expert with R
 // rows has ceil(R / 16) <= R / 16 + 1 groups, at most min(E, m k) experts
 // are hit, and the shared expert adds ceil(m / 16).
-static int group_cap(const Params &p, int m)
+static int group_cap(const Params &p, int m, int rows = kGroupRows)
 {
     const int np = m * p.k;
-    return std::min(p.E, np) + (np + kGroupRows - 1) / kGroupRows +
-           (p.has_shared ? (m + kGroupRows - 1) / kGroupRows : 0);
+    return std::min(p.E, np) + (np + rows - 1) / rows + (p.has_shared ? (m + rows - 1) / rows : 0);
 }
+
+// From this many tokens on the prefill kernels run (64-row groups, one decode
+// per 64 rows), unless a tensor has 6-bit codes (the persistent kernel serves
+// those at every m). Below it the persistent kernel is as fast or faster:
+// measured on the 4096 x 2048 layer with Zipf routing, per layer, persistent
+// vs prefill: m = 64 249 vs 277 us, 128 370 vs 371, 256 570 vs 483, 512 959
+// vs 686.
+constexpr int kPrefillFrom = 128;
 
 static moe_status validate(const moe_decode_config *c)
 {
@@ -273,6 +282,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     h->lds.assign(M + 1, 0);
     h->span1.assign(M + 1, 1);
     h->gcap.assign(M + 1, 0);
+    h->prefill.assign(M + 1, 0);
     h->lds_tab.assign(M + 1, 0);
     for (int m = 1; m <= (int)M; ++m) {
         h->span1[m] = (m >= 8 && p.n_rb1 % 2 == 0) ? 2 : 1;
@@ -281,6 +291,7 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
         const size_t stage = ((size_t)std::min(m, kGroupRows) * (kc + kLdsPadHalves) *
                                   sizeof(_Float16) + 15) & ~size_t(15);
         h->gcap[m] = group_cap(p, m);
+        h->prefill[m] = m >= kPrefillFrom && !p.has6;
         h->lds_tab[m] = (int)stage;
         const size_t lds = stage + 3 * sizeof(int) * (size_t)h->gcap[m];
         int bpc = 0;
@@ -322,15 +333,23 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
     p.span1 = h->span1[m];
     p.gcap = h->gcap[m];
     p.lds_tab = h->lds_tab[m];
+    const bool pf = h->prefill[m] != 0;
+    p.group_rows = pf ? kPrefillRows : kGroupRows;
     HIP_TRY(launch_route(p, (const uint16_t *)x_bf16, logits, m, s));
     if (h->ev_begin)
         HIP_TRY(hipEventRecord(h->ev_begin, s));
-    HIP_TRY(launch_expert(p, h->grid[m], h->lds[m], s));
+    if (pf) {
+        HIP_TRY(launch_prefill(p, group_cap(p, m, kPrefillRows), s));
+        p.ks2 = 1;  // y written whole: one split for the combine
+    } else {
+        HIP_TRY(launch_expert(p, h->grid[m], h->lds[m], s));
+    }
     if (h->ev_end)
         HIP_TRY(hipEventRecord(h->ev_end, s));
     HIP_TRY(launch_combine(p, m, s));
     h->ran = true;
     h->last_m = m;
+    h->last_prefill = pf;
     return MOE_OK;
 }
 
@@ -399,7 +418,8 @@ extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_
         moe_decode_stats st{};
         st.m = plan.m;
         st.hit_experts = plan.n_hit;
-        st.items = plan.n_items;
+        // prefill: one item per (row group, output row block) of each kernel
+        st.items = h->last_prefill ? plan.n_groups * (p.n_rb1 + p.H / 256) : plan.n_items;
         uint32_t done = 0;
         for (int i = 0; i < kDoneSlots; ++i)
             done += c.items_done[i];

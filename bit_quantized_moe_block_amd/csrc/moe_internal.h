@@ -48,7 +48,7 @@ struct Plan {
     int32_t pad[2];
     int32_t g_expert[kMaxGroups];  // expert of group u (groups in expert order)
     int32_t g_off[kMaxGroups];     // first row of u in the bucket row list
-    int32_t g_rows[kMaxGroups];    // rows of u (1..16)
+    int32_t g_rows[kMaxGroups];    // rows of u (1..group_rows)
 };
 
 // Completed work items are counted on kDoneSlots counters (block b adds to
@@ -76,6 +76,7 @@ struct Params {
                            // rows m*k + t, group expert id E)
     int32_t sh_half;       // 1: the shared expert's items cover half row blocks (its
                            // 6-bit codes make a full row block three 2-bit ones)
+    int32_t group_rows;    // rows per row group: 16 (persistent decode kernel) or 64 (prefill)
     int32_t gcap;          // row-group table entries in LDS (bound on the groups of a run)
     int32_t lds_tab;       // byte offset of that table in the expert kernel's dynamic LDS
     uint32_t spin_limit;   // polls before a dependency wait gives up
@@ -106,6 +107,10 @@ hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits,
                         hipStream_t s);
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const Params &p, int m, hipStream_t s);
+// Prefill kernels (gate/up, then down) over up to grid_groups row groups of
+// up to 64 rows.
+hipError_t launch_prefill(const Params &p, int grid_groups, hipStream_t s);
+constexpr int kPrefillRows = 64;  // rows per prefill row group
 // Occupancy of the expert kernel for a given dynamic LDS size.
 hipError_t expert_occupancy(int format, int ng, bool six, int *blocks_per_cu, size_t lds_bytes);
 

@@ -321,15 +321,20 @@ def test_nvfp4_full_sampled(m):
     parity(case, tokens=sorted(set([0, m - 1])), max_tokens=8)
 
 
-# Large m (prefill / batched verify, up to 512 tokens): the same kernels with
-# many row groups per expert. Zipf routing sends hundreds of rows to the hot
-# experts (tens of 16-row groups each).
+# Large m (prefill / batched verify, up to 512 tokens): 33 and 100 tokens on
+# the persistent kernel (16-row groups), from 128 tokens on the prefill
+# kernels (row groups of up to 64 rows, odd and even column-chunk counts,
+# NVFP4, a 3-bit shared expert); with a 6-bit tensor the persistent kernel at
+# any m. Zipf routing sends hundreds of rows to the hot experts.
 LARGE_M = [
     (small_workload("lm1", 16, 4, 256, 128, bits_mix="alternate", router="zipf", config_id=401), 33),
     (small_workload("lm2", 32, 8, 512, 256, bits_mix="all3", router="zipf", config_id=402), 100),
     (small_workload("lm3", 64, 8, 512, 256, bits_mix="alternate", config_id=403), 257),
     (small_workload("lm4", 16, 2, 256, 128, bits_mix="all2", router="zipf", config_id=404), 512),
     (small_workload("lm5", 32, 4, 256, 128, bits_mix="alternate", config_id=405, shared_bits=6), 300),
+    (small_workload("lm6", 16, 4, 512, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=406), 200),
+    (small_workload("lm7", 16, 2, 512, 256, bits_mix="all3", router="zipf", config_id=407,
+                    shared_bits=3), 150),
 ]
 
 
