@@ -256,9 +256,14 @@ __device__ void bucket_block(const Params &p, int m)
     // are the tokens of its bitmask (bit t % 32 of word t / 32), ascending by
     // t; the rank of (t, j) inside e's bucket is the count of mask bits below t.
     const int np = m * k;
+    // the first two pairs of each thread stay in registers for the ranks below
+    // (m * k <= 512 needs no second load)
+    int e_keep[2] = {0, 0};
     for (int i = tid; i < np; i += kRouteThreads) {
-        const int t = i / k;
-        atomicOr(&s_mask[ld_coherent_i32(&p.ids[i]) * W + (t >> 5)], 1u << (t & 31));
+        const int t = i / k, e = ld_coherent_i32(&p.ids[i]);
+        if (i < 2 * kRouteThreads)
+            e_keep[i / kRouteThreads] = e;
+        atomicOr(&s_mask[e * W + (t >> 5)], 1u << (t & 31));
     }
     __syncthreads();
     int cnt = 0;
@@ -267,7 +272,6 @@ __device__ void bucket_block(const Params &p, int m)
             cnt += __popc(s_mask[tid * W + w]);
     const int GR = p.group_rows;  // rows per row group: 16 (decode) or 64 (prefill)
     const int ng_e = (cnt + GR - 1) / GR;
-    const int nhit = __syncthreads_count(cnt > 0);
     // one scan of (rows | groups << 16): rows <= 8192, groups <= 768
     int packed_total;
     const int packed = block_excl_scan(cnt | (ng_e << 16), tmp, packed_total);
@@ -300,7 +304,8 @@ __device__ void bucket_block(const Params &p, int m)
     }
     __syncthreads();
     for (int i = tid; i < np; i += kRouteThreads) {
-        const int e = ld_coherent_i32(&p.ids[i]), t = i / k;
+        const int e = i < 2 * kRouteThreads ? e_keep[i / kRouteThreads] : ld_coherent_i32(&p.ids[i]);
+        const int t = i / k;
         const int q = s_base[e * W + (t >> 5)] + __popc(s_mask[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
         p.rows[q] = i;
         p.pos[i] = q;
@@ -309,7 +314,6 @@ __device__ void bucket_block(const Params &p, int m)
         p.offsets[E] = total;
         const int n1 = ngs * shared_items(p, false) + ngroups * (p.n_rb1 / p.span1) * p.ks1;
         P->m = m;
-        P->n_hit = nhit;
         P->n_groups = ngroups + ngs;
         P->n_sgroups = ngs;
         P->n_items1 = n1;

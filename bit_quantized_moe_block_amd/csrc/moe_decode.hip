@@ -417,7 +417,11 @@ extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_
         HIP_TRY(hipMemcpy(&c, p.ctr, sizeof c, hipMemcpyDeviceToHost));
         moe_decode_stats st{};
         st.m = plan.m;
-        st.hit_experts = plan.n_hit;
+        std::vector<int32_t> counts(p.E);
+        HIP_TRY(hipMemcpy(counts.data(), p.counts, 4 * p.E, hipMemcpyDeviceToHost));
+        st.hit_experts = 0;
+        for (int32_t c : counts)
+            st.hit_experts += c > 0;
         // prefill: one item per (row group, output row block) of each kernel
         st.items = h->last_prefill ? plan.n_groups * (p.n_rb1 + p.H / 256) : plan.n_items;
         uint32_t done = 0;

@@ -37,15 +37,14 @@ struct DevTensor {
     int32_t bits;
 };
 
-// Routing result of one run, written by block 0 of the route kernel.
+// Routing result of one run, written by the route kernel's bucketing block.
 struct Plan {
     int32_t m;
-    int32_t n_hit;         // experts with >= 1 row
-    int32_t n_groups;      // row groups (<= 16 rows each)
+    int32_t n_groups;      // row groups (<= group_rows rows each)
     int32_t n_items1;      // gate/up work items
     int32_t n_items;       // all work items
     int32_t n_sgroups;     // row groups of the shared expert (groups 0 .. n_sgroups-1)
-    int32_t pad[2];
+    int32_t pad[3];
     int32_t g_expert[kMaxGroups];  // expert of group u (groups in expert order)
     int32_t g_off[kMaxGroups];     // first row of u in the bucket row list
     int32_t g_rows[kMaxGroups];    // rows of u (1..group_rows)
