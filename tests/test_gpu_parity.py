@@ -365,3 +365,53 @@ def test_prefill_layer_sampled_and_repeatable():
         assert err <= REL_TOL
     finally:
         dl.close()
+
+
+def test_one_handle_both_paths_and_graph_replay():
+    # One handle (max_tokens 300) alternating the prefill kernels (m = 256)
+    # and the persistent kernel (m = 100): eager runs are bit-identical to
+    # each other, and a graph holding both runs replays to the same bytes
+    # with eager work in between; m = 256 matches the oracle.
+    w = small_workload("both", 16, 4, 512, 256, bits_mix="alternate", router="zipf",
+                       config_id=408)
+    cases = {m: gen.make_case(w, m) for m in (256, 100)}
+    say("[graph] prefill and persistent paths on one handle")
+    s = torch.cuda.Stream()
+    layer = DeviceLayer.from_case(cases[256], max_tokens=300)
+    try:
+        dev = {m: to_dev(c) for m, c in cases.items()}
+        ref = {}
+        with torch.cuda.stream(s):
+            for rep in range(2):
+                for m in (256, 100):
+                    x, lg, out = dev[m]
+                    out.fill_(float("nan"))
+                    layer.run(x, lg, out, stream=s)
+                    s.synchronize()
+                    if rep == 0:
+                        ref[m] = out.clone()
+                    else:
+                        assert torch.equal(out.view(torch.int32), ref[m].view(torch.int32)), m
+        outs_g = {m: torch.full_like(dev[m][2], float("nan")) for m in dev}
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for m in (256, 100):
+                layer.run(dev[m][0], dev[m][1], outs_g[m], stream=s)
+        for rep in range(3):
+            for o in outs_g.values():
+                o.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            for m in dev:
+                assert torch.equal(outs_g[m].view(torch.int32), ref[m].view(torch.int32)), (rep, m)
+            with torch.cuda.stream(s):
+                x, lg, out = dev[100]
+                layer.run(x, lg, out, stream=s)
+            s.synchronize()
+            assert torch.equal(out.view(torch.int32), ref[100].view(torch.int32))
+        r = oracle.Layer.from_case(cases[256]).run(cases[256]["x"], cases[256]["logits"])
+        err = rel_err(ref[256].cpu().numpy(), r["out"])
+        say(f"    rel={err:.3e}")
+        assert err <= REL_TOL
+    finally:
+        layer.close()

@@ -249,7 +249,7 @@ def test_route_matches_stable_argsort_and_sums_to_one():
 
 def test_bucket_matches_numpy():
     rng = np.random.default_rng(4)
-    for m, E, k in [(1, 8, 2), (24, 256, 8), (5, 16, 3)]:
+    for m, E, k in [(1, 8, 2), (24, 256, 8), (5, 16, 3), (300, 16, 4), (512, 256, 8)]:
         logits = rng.standard_normal((m, E)).astype(np.float32)
         ids, _ = oracle.route(logits, k)
         b = oracle.bucket(ids, E)
