@@ -143,8 +143,12 @@ moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
  * returns MOE_E_STREAM (page "LNA-CANON.md", "lna2 とは": concurrent streams
  * are forbidden; page "lna-lab/README.md", "The three traps", item 3: two
  * streams sharing one lock buffer deadlocked). Results are bitwise identical
- * for identical inputs. Errors: MOE_E_INVALID, MOE_E_STREAM, MOE_E_HIP
- * (launch failure). Device faults surface at the caller's next sync.
+ * for identical inputs (same m). From m = 128 on (without 6-bit tensors) the
+ * step runs grouped-GEMM prefill kernels instead of the persistent decode
+ * kernel (page "LNA-CANON.md", section "起動": prefill batches of up to 512
+ * tokens); a token's output then differs from a run at smaller m in rounding
+ * only. Errors: MOE_E_INVALID, MOE_E_STREAM, MOE_E_HIP (launch failure).
+ * Device faults surface at the caller's next sync.
  */
 moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits, float *out,
                           int32_t m, void *hip_stream);
