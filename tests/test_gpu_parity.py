@@ -335,6 +335,11 @@ LARGE_M = [
     (small_workload("lm6", 16, 4, 512, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=406), 200),
     (small_workload("lm7", 16, 2, 512, 256, bits_mix="all3", router="zipf", config_id=407,
                     shared_bits=3), 150),
+    # the largest pair count (512 tokens x top-16 = 8192 rows, 256 experts)
+    # and top-16 on the persistent kernel
+    (small_workload("lm8", 256, 16, 256, 128, bits_mix="alternate", router="zipf",
+                    config_id=409), 512),
+    (small_workload("lm9", 32, 16, 256, 128, bits_mix="alternate", config_id=410), 100),
 ]
 
 
