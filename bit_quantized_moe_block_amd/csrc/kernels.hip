@@ -1308,17 +1308,18 @@ struct PfStage {
     }
 };
 
-// One 128-column group of the wave's kPfNT tiles against the nsub staged
+// One 128-column group of the wave's kPfNT tiles against the four staged
 // 16-row subtiles (A, B and result layouts as in process_group; subtile t =
 // rows 16t .. 16t+15). Per step: the subtiles' A operands, then per tile one
-// decode and nsub MFMAs. The group scale multiplies the decoded fp16 weights
+// decode and four MFMAs. A group with fewer rows still runs all four: its
+// staged rows past R repeat row R-1 and their results are never stored, and
+// per-subtile branches cost more issue slots than the MFMAs they skip. The group scale multiplies the decoded fp16 weights
 // (one more fp16 rounding, as the NVFP4 block scale), so the accumulators
 // take the products directly: per-group partial results for every (tile,
 // subtile) would not fit in the registers.
 template <int CLASS, int FMT>
 __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const _Float16 *A,
-                                         int nsub, const uint32_t (&tab)[4],
-                                         floatx4 (&acc)[kPfNT][kPfSub])
+                                         const uint32_t (&tab)[4], floatx4 (&acc)[kPfNT][kPfSub])
 {
     const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -1326,8 +1327,7 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
         half8 a[kPfSub];
 #pragma unroll
         for (int t = 0; t < kPfSub; ++t)
-            a[t] = t < nsub ? *(const half8 *)(A + (16 * t + r16) * kPfAStride + q * 32 + s * 8)
-                            : half8{};
+            a[t] = *(const half8 *)(A + (16 * t + r16) * kPfAStride + q * 32 + s * 8);
 #pragma unroll
         for (int i = 0; i < kPfNT; ++i) {
             half2v bs = half2v{1, 1};
@@ -1343,63 +1343,21 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
             }
 #pragma unroll
             for (int t = 0; t < kPfSub; ++t)
-                if (t < nsub)
-                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
         }
     }
 }
 
-template <int CLASS>
-__device__ __forceinline__ void pf_group_any(const GroupBuf<CLASS, kPfNT> &b, int bits,
-                                             const _Float16 *A, int nsub, const uint32_t (&tab)[4],
-                                             floatx4 (&acc)[kPfNT][kPfSub])
+// The main loop and epilogue of a prefill block, for one code format: FMT =
+// codebook bits (2 or 3, the row group's expert) or 4 (NVFP4). One decode
+// path per instance keeps the loop inside the register budget.
+template <int CLASS, bool DOWN, int FMT>
+__device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const WaveJob &J, int off,
+                                       int R, int tok, int rb, int wave, int sc_lane)
 {
-    if constexpr (!is_cb<CLASS>)
-        pf_group<CLASS, 4>(b, A, nsub, tab, acc);
-    else if (bits == 3)
-        pf_group<CLASS, 3>(b, A, nsub, tab, acc);
-    else
-        pf_group<CLASS, 2>(b, A, nsub, tab, acc);
-}
-
-// Block b: row group u = b / RB, output row block rb = b % RB (RB = I / 128
-// gate/up blocks, H / 256 down blocks); blocks past the run's groups exit.
-// The chunks of the activations go through two LDS halves and the weight
-// groups through two register buffers: chunk c+1's activations and weight
-// group c+2 load while chunk c is computed.
-template <int CLASS, bool DOWN>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void prefill_kernel(Params p)
-{
-    extern __shared__ _Float16 pf_lds[];  // [2][64][kPfAStride]; the gate/up epilogue reuses it
-    const Plan *P = p.plan;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = uniform(tid >> 6);
+    constexpr int KB = FMT == 4 ? 0 : FMT;
+    const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, q = lane >> 4;
-    const int RB = DOWN ? p.H / 256 : p.n_rb1;
-    const int u = blockIdx.x / RB, rb = blockIdx.x - u * RB;
-    if (u >= uniform(P->n_groups))
-        return;
-    const int e = uniform(P->g_expert[u]), off = uniform(P->g_off[u]), R = uniform(P->g_rows[u]);
-    const int m = uniform(P->m);
-    const int nsub = (R + 15) >> 4;
-    int tok = 0;  // gate/up: token of row `lane` of the group
-    if (!DOWN) {
-        const int qrow = off + min(lane, R - 1);
-        tok = qrow < m * p.k ? p.rows[qrow] / p.k : qrow - m * p.k;
-    }
-    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave >> 2)];
-    WaveJob J;
-    J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
-    J.scales = (gu8p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.scales);
-    J.lut = (const uint16_t *)(uintptr_t)uniform((uint64_t)(uintptr_t)d.lut);
-    J.ts = __uint_as_float((uint32_t)uniform((int)__float_as_uint(d.tensor_scale)));
-    J.bits = uniform(d.bits);
-    J.G = DOWN ? p.I / 128 : p.H / 128;
-    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 3) * kPfNT;
-    J.g0 = 0;
-    const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
-
     uint32_t tab[4] = {0, 0, 0, 0};
     u32x4 lut = u32x4{0, 0, 0, 0};
     if constexpr (is_cb<CLASS>)
@@ -1412,9 +1370,9 @@ void prefill_kernel(Params p)
     PfStage st;
     const int G1 = J.G - 1;
     st.issue(p, DOWN, off, R, tok, 0);
-    load_group<CLASS, 0, kPfNT>(bA, J, 0, lane, sc_lane);
+    load_group<CLASS, KB, kPfNT>(bA, J, 0, lane, sc_lane);
     st.commit(pf_lds);
-    load_group<CLASS, 0, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
+    load_group<CLASS, KB, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
     __syncthreads();
     if constexpr (is_cb<CLASS>)
         lut_tables(lut, tab);
@@ -1433,8 +1391,8 @@ void prefill_kernel(Params p)
         _Float16 *Anext = (c & 1) ? half0 : half1;
         st.issue(p, DOWN, off, R, tok, min(c + 1, G1));
         if (c < J.G)
-            pf_group_any<CLASS>(b, J.bits, A, nsub, tab, acc);
-        load_group<CLASS, 0, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
+            pf_group<CLASS, FMT>(b, A, tab, acc);
+        load_group<CLASS, KB, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
         st.commit(Anext);
         __syncthreads();
     };
@@ -1460,7 +1418,7 @@ void prefill_kernel(Params p)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * t + 4 * q + j;
-                    if (t < nsub && row < R)
+                    if (row < R)
                         p.y_part[(size_t)(off + row) * p.H + n0 + 16 * i + r16] = acc[i][t][j];
                 }
     } else {
@@ -1476,7 +1434,7 @@ void prefill_kernel(Params p)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * t + 4 * q + j;
-                        if (t < nsub && row < R)
+                        if (row < R)
                             hb[row * kPfHStride + lr0 + 16 * i + r16] = acc[i][t][j];
                     }
         __syncthreads();
@@ -1488,7 +1446,7 @@ void prefill_kernel(Params p)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * t + 4 * q + j;
-                        if (t < nsub && row < R) {
+                        if (row < R) {
                             float *hp = hb + row * kPfHStride + lr0 + 16 * i + r16;
                             const float g = acc[i][t][j];
                             *hp = g / (1.0f + expf(-g)) * *hp;
@@ -1508,6 +1466,51 @@ void prefill_kernel(Params p)
             *(half2v *)(p.hr + (size_t)(off + row) * p.I + n) = half2v{(_Float16)v0, (_Float16)v1};
         }
     }
+}
+
+// Block b: row group u = b / RB, output row block rb = b % RB (RB = I / 128
+// gate/up blocks, H / 256 down blocks); blocks past the run's groups exit.
+// The chunks of the activations go through two LDS halves and the weight
+// groups through two register buffers: chunk c+1's activations and weight
+// group c+2 load while chunk c is computed.
+template <int CLASS, bool DOWN>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void prefill_kernel(Params p)
+{
+    extern __shared__ _Float16 pf_lds[];  // [2][64][kPfAStride]; the gate/up epilogue reuses it
+    const Plan *P = p.plan;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int RB = DOWN ? p.H / 256 : p.n_rb1;
+    const int u = blockIdx.x / RB, rb = blockIdx.x - u * RB;
+    if (u >= uniform(P->n_groups))
+        return;
+    const int e = uniform(P->g_expert[u]), off = uniform(P->g_off[u]), R = uniform(P->g_rows[u]);
+    const int m = uniform(P->m);
+    int tok = 0;  // gate/up: token of row `lane` of the group
+    if (!DOWN) {
+        const int qrow = off + min(lane, R - 1);
+        tok = qrow < m * p.k ? p.rows[qrow] / p.k : qrow - m * p.k;
+    }
+    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave >> 2)];
+    WaveJob J;
+    J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
+    J.scales = (gu8p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.scales);
+    J.lut = (const uint16_t *)(uintptr_t)uniform((uint64_t)(uintptr_t)d.lut);
+    J.ts = __uint_as_float((uint32_t)uniform((int)__float_as_uint(d.tensor_scale)));
+    J.bits = uniform(d.bits);
+    J.G = DOWN ? p.I / 128 : p.H / 128;
+    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 3) * kPfNT;
+    J.g0 = 0;
+    const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+
+    if constexpr (!is_cb<CLASS>)
+        pf_run<CLASS, DOWN, 4>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    else if (J.bits == 3)
+        pf_run<CLASS, DOWN, 3>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    else
+        pf_run<CLASS, DOWN, 2>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
     if (tid == 0)
         atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], 1u);
 }
