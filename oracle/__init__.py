@@ -15,8 +15,10 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_SOURCE / MOE_ORACLE_LIBRARY: build and load another copy of the C
+# source (the mutation test plants mistakes in a copy this way).
+_SRC = os.environ.get("MOE_ORACLE_SOURCE") or os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.environ.get("MOE_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 FMT_CODEBOOK = 1
 FMT_NVFP4 = 2
