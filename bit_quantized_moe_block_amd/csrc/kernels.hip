@@ -1308,20 +1308,44 @@ struct PfStage {
     }
 };
 
+// Two fp16 values packed in w, each times f (fp16). The word comes in as a
+// value: a bit cast applied to a vector element in place has been compiled
+// to read the vector's first element.
+__device__ __forceinline__ uint32_t scale_pair(uint32_t w, _Float16 f)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, w) * half2v{f, f});
+}
+
 // One 128-column group of the wave's kPfNT tiles against the four staged
 // 16-row subtiles (A, B and result layouts as in process_group; subtile t =
 // rows 16t .. 16t+15). Per step: the subtiles' A operands, then per tile one
 // decode and four MFMAs. A group with fewer rows still runs all four: its
 // staged rows past R repeat row R-1 and their results are never stored, and
-// per-subtile branches cost more issue slots than the MFMAs they skip. The group scale multiplies the decoded fp16 weights
-// (one more fp16 rounding, as the NVFP4 block scale), so the accumulators
-// take the products directly: per-group partial results for every (tile,
-// subtile) would not fit in the registers.
+// per-subtile branches cost more issue slots than the MFMAs they skip. The
+// decoded weights carry the group scale already (fp16 entry x scale, one more
+// fp16 rounding, as the NVFP4 block scale), so the accumulators take the
+// products directly: per-group partial results for every (tile, subtile)
+// would not fit in the registers.
 template <int CLASS, int FMT>
 __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const _Float16 *A,
-                                         const uint32_t (&tab)[4], floatx4 (&acc)[kPfNT][kPfSub])
+                                         const u32x4 lut, floatx4 (&acc)[kPfNT][kPfSub])
 {
     const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+    // codebook: the lane's tile tables hold codebook entry x group scale
+    // (fp16), so a lookup yields the scaled weight: the same fp16 value as
+    // scaling each decoded weight, for 2 (K = 2) or 4 (K = 3) multiplies and
+    // the byte split per tile and group instead of four per decoded step
+    uint32_t tab[kPfNT][4] = {};
+    if constexpr (FMT != 4)
+#pragma unroll
+        for (int i = 0; i < kPfNT; ++i) {
+            const _Float16 f = __builtin_bit_cast(_Float16, (uint16_t)b.sc[i]);
+            u32x4 sl = u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < (FMT == 3 ? 4 : 2); ++k)
+                sl[k] = scale_pair(lut[k], f);
+            lut_tables(sl, tab[i]);
+        }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         half8 a[kPfSub];
@@ -1336,11 +1360,7 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
                                                     : __builtin_amdgcn_cvt_f32_fp8(b.sc[i], 1));
                 bs = half2v{v, v};
             }
-            half8 bv = decode_step<FMT>(b.w[i], s, tab, bs);
-            if constexpr (FMT != 4) {
-                const _Float16 f = __builtin_bit_cast(_Float16, (uint16_t)b.sc[i]);
-                bv *= half8{f, f, f, f, f, f, f, f};
-            }
+            const half8 bv = decode_step<FMT>(b.w[i], s, tab[i], bs);
 #pragma unroll
             for (int t = 0; t < kPfSub; ++t)
                 acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
@@ -1358,7 +1378,6 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     constexpr int KB = FMT == 4 ? 0 : FMT;
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, q = lane >> 4;
-    uint32_t tab[4] = {0, 0, 0, 0};
     u32x4 lut = u32x4{0, 0, 0, 0};
     if constexpr (is_cb<CLASS>)
         lut = load_lut_raw(J);
@@ -1374,8 +1393,6 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     st.commit(pf_lds);
     load_group<CLASS, KB, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
     __syncthreads();
-    if constexpr (is_cb<CLASS>)
-        lut_tables(lut, tab);
 
     floatx4 acc[kPfNT][kPfSub];
 #pragma unroll
@@ -1391,7 +1408,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
         _Float16 *Anext = (c & 1) ? half0 : half1;
         st.issue(p, DOWN, off, R, tok, min(c + 1, G1));
         if (c < J.G)
-            pf_group<CLASS, FMT>(b, A, tab, acc);
+            pf_group<CLASS, FMT>(b, A, lut, acc);
         load_group<CLASS, KB, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
         st.commit(Anext);
         __syncthreads();
