@@ -420,3 +420,27 @@ def test_one_handle_both_paths_and_graph_replay():
         assert err <= REL_TOL
     finally:
         layer.close()
+
+
+def test_nvfp4_prefill_layer_sampled():
+    # The full NVFP4 layer (256 experts, 4096 x 2048) at m = 256 on the
+    # prefill kernels: exact routing, three tokens against the oracle, and a
+    # second run bit-identical.
+    w = WORKLOADS["nvfp4"]
+    m = 256
+    case = gen.make_case(w, m)
+    tokens = [0, 128, 255]
+    say(f"[parity] nvfp4 prefill m={m}")
+    dl = DeviceLayer.from_case(case, max_tokens=m)
+    try:
+        out = run_gpu(dl, case)
+        check_routing(dl, case, m)
+        st = dl.stats()
+        assert st.error_word == 0 and st.items_done == st.items
+        assert np.array_equal(out, run_gpu(dl, case))
+        ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+        err = rel_err(out, ref["out"], tokens)
+        say(f"    rel={err:.3e} hit={st.hit_experts} items={st.items}")
+        assert err <= REL_TOL
+    finally:
+        dl.close()
