@@ -1326,9 +1326,9 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t w, _Float16 f)
 // fp16 rounding, as the NVFP4 block scale), so the accumulators take the
 // products directly: per-group partial results for every (tile, subtile)
 // would not fit in the registers.
-template <int CLASS, int FMT>
+template <int CLASS, int FMT, int NSUB>
 __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const _Float16 *A,
-                                         const u32x4 lut, floatx4 (&acc)[kPfNT][kPfSub])
+                                         const u32x4 lut, floatx4 (&acc)[kPfNT][NSUB])
 {
     const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
     // codebook: the lane's tile tables hold codebook entry x group scale
@@ -1348,9 +1348,9 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
         }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        half8 a[kPfSub];
+        half8 a[NSUB];
 #pragma unroll
-        for (int t = 0; t < kPfSub; ++t)
+        for (int t = 0; t < NSUB; ++t)
             a[t] = *(const half8 *)(A + (16 * t + r16) * kPfAStride + q * 32 + s * 8);
 #pragma unroll
         for (int i = 0; i < kPfNT; ++i) {
@@ -1362,7 +1362,7 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
             }
             const half8 bv = decode_step<FMT>(b.w[i], s, tab[i], bs);
 #pragma unroll
-            for (int t = 0; t < kPfSub; ++t)
+            for (int t = 0; t < NSUB; ++t)
                 acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
         }
     }
@@ -1371,7 +1371,7 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
 // The main loop and epilogue of a prefill block, for one code format: FMT =
 // codebook bits (2 or 3, the row group's expert) or 4 (NVFP4). One decode
 // path per instance keeps the loop inside the register budget.
-template <int CLASS, bool DOWN, int FMT>
+template <int CLASS, bool DOWN, int FMT, int NSUB>
 __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const WaveJob &J, int off,
                                        int R, int tok, int rb, int wave, int sc_lane)
 {
@@ -1394,11 +1394,11 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     load_group<CLASS, KB, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
     __syncthreads();
 
-    floatx4 acc[kPfNT][kPfSub];
+    floatx4 acc[kPfNT][NSUB];
 #pragma unroll
     for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
-        for (int t = 0; t < kPfSub; ++t)
+        for (int t = 0; t < NSUB; ++t)
             acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     _Float16 *const half0 = pf_lds, *const half1 = pf_lds + kPfRows * kPfAStride;
     // chunk c: weights from buffer c % 2 (refilled with chunk c + 2),
@@ -1408,7 +1408,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
         _Float16 *Anext = (c & 1) ? half0 : half1;
         st.issue(p, DOWN, off, R, tok, min(c + 1, G1));
         if (c < J.G)
-            pf_group<CLASS, FMT>(b, A, lut, acc);
+            pf_group<CLASS, FMT, NSUB>(b, A, lut, acc);
         load_group<CLASS, KB, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
         st.commit(Anext);
         __syncthreads();
@@ -1421,7 +1421,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
 #pragma unroll
         for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
-            for (int t = 0; t < kPfSub; ++t)
+            for (int t = 0; t < NSUB; ++t)
                 acc[i][t] *= J.ts;
 
     // result layout: lane holds rows 16t + 4q + j (j = 0..3) of subtile t,
@@ -1431,7 +1431,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
 #pragma unroll
         for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
-            for (int t = 0; t < kPfSub; ++t)
+            for (int t = 0; t < NSUB; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * t + 4 * q + j;
@@ -1447,7 +1447,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
 #pragma unroll
             for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
-                for (int t = 0; t < kPfSub; ++t)
+                for (int t = 0; t < NSUB; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * t + 4 * q + j;
@@ -1459,7 +1459,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
 #pragma unroll
             for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
-                for (int t = 0; t < kPfSub; ++t)
+                for (int t = 0; t < NSUB; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int row = 16 * t + 4 * q + j;
@@ -1483,6 +1483,19 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
             *(half2v *)(p.hr + (size_t)(off + row) * p.I + n) = half2v{(_Float16)v0, (_Float16)v1};
         }
     }
+}
+
+// The loop instance for the group's code width and subtile count.
+template <int CLASS, bool DOWN, int NSUB>
+__device__ __forceinline__ void pf_dispatch(const Params &p, _Float16 *pf_lds, const WaveJob &J,
+                                            int off, int R, int tok, int rb, int wave, int sc_lane)
+{
+    if constexpr (!is_cb<CLASS>)
+        pf_run<CLASS, DOWN, 4, NSUB>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    else if (J.bits == 3)
+        pf_run<CLASS, DOWN, 3, NSUB>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    else
+        pf_run<CLASS, DOWN, 2, NSUB>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
 }
 
 // Block b: row group u = b / RB, output row block rb = b % RB (RB = I / 128
@@ -1522,12 +1535,12 @@ void prefill_kernel(Params p)
     J.g0 = 0;
     const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
 
-    if constexpr (!is_cb<CLASS>)
-        pf_run<CLASS, DOWN, 4>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
-    else if (J.bits == 3)
-        pf_run<CLASS, DOWN, 3>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    // groups of up to 16 rows (most experts at Zipf routing) take one MFMA
+    // subtile, larger groups all four
+    if (R <= 16)
+        pf_dispatch<CLASS, DOWN, 1>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
     else
-        pf_run<CLASS, DOWN, 2>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+        pf_dispatch<CLASS, DOWN, kPfSub>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
     if (tid == 0)
         atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], 1u);
 }
