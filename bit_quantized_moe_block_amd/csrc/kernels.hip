@@ -1535,10 +1535,14 @@ void prefill_kernel(Params p)
     J.g0 = 0;
     const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
 
-    // groups of up to 16 rows (most experts at Zipf routing) take one MFMA
-    // subtile, larger groups all four
+    // one MFMA subtile per 16 rows of the group: groups of up to 16 rows are
+    // most experts at Zipf routing, 17 .. 48 rows the tails of hot experts
     if (R <= 16)
         pf_dispatch<CLASS, DOWN, 1>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    else if (R <= 32)
+        pf_dispatch<CLASS, DOWN, 2>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
+    else if (R <= 48)
+        pf_dispatch<CLASS, DOWN, 3>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
     else
         pf_dispatch<CLASS, DOWN, kPfSub>(p, pf_lds, J, off, R, tok, rb, wave, sc_lane);
     if (tid == 0)
