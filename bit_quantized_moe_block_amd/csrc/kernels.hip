@@ -187,10 +187,12 @@ __device__ __forceinline__ int ld_coherent_i32(const int32_t *p)
 }
 
 // Top-k of token t by one wave; lane holds experts lane + 64 i. Each round
-// takes the largest key, then the lowest expert id among equal keys; lane j
-// keeps slot j. Weights: softmax over the k selected logits, the denominator
-// summed in slot order. ids go out agent-coherent for the bucketing block.
-__device__ void route_token(const Params &p, const float *__restrict__ logits, int t)
+// takes the largest key, then the lowest expert id among equal keys (the
+// lowest i with a match, then the lowest lane: one ballot per i, no second
+// reduction); lane j keeps slot j. Weights: softmax over the k selected
+// logits, the denominator summed in slot order. ids go out agent-coherent for
+// the bucketing block, and to s_ids (if given) for a bucketing in this block.
+__device__ void route_token(const Params &p, const float *__restrict__ logits, int t, int *s_ids)
 {
     const int lane = threadIdx.x & 63;
     const int E = p.E, k = p.k;
@@ -204,12 +206,14 @@ __device__ void route_token(const Params &p, const float *__restrict__ logits, i
     uint32_t my_key = 0;
     for (int j = 0; j < k; ++j) {
         const uint32_t kmax = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-        uint32_t cand = 0xFFFFFFFFu;
+        int e = 0;
 #pragma unroll
-        for (int i = 3; i >= 0; --i)
-            if (key[i] == kmax)
-                cand = lane + 64 * i;
-        const int e = (int)~wave_max_u32(~cand);
+        for (int i = 3; i >= 0; --i) {
+            const uint64_t hit = __ballot(key[i] == kmax);
+            if (hit)
+                e = 64 * i + __builtin_ctzll(hit);
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (e == lane + 64 * i)
@@ -227,6 +231,8 @@ __device__ void route_token(const Params &p, const float *__restrict__ logits, i
     if (lane < k) {
         st_coherent((uint32_t *)&p.ids[t * k + lane], (uint32_t)my_id);
         p.wts[t * k + lane] = ex / den;
+        if (s_ids)
+            s_ids[t * k + lane] = my_id;
     }
 }
 
@@ -240,7 +246,7 @@ size_t route_lds_bytes(int E, int m)
 // The last top-k block to finish builds the buckets: per-expert rows, row
 // groups (<= p.group_rows rows each), the work plan, and clears the expert kernel's
 // counters (every run and every graph replay starts clean without a memset).
-__device__ void bucket_block(const Params &p, int m)
+__device__ void bucket_block(const Params &p, int m, const int *s_ids)
 {
     extern __shared__ uint32_t s_route[];  // [E][W] token masks, then [E][W] row bases
     __shared__ int tmp[kRouteWaves];
@@ -260,7 +266,7 @@ __device__ void bucket_block(const Params &p, int m)
     // (m * k <= 512 needs no second load)
     int e_keep[2] = {0, 0};
     for (int i = tid; i < np; i += kRouteThreads) {
-        const int t = i / k, e = ld_coherent_i32(&p.ids[i]);
+        const int t = i / k, e = s_ids ? s_ids[i] : ld_coherent_i32(&p.ids[i]);
         if (i < 2 * kRouteThreads)
             e_keep[i / kRouteThreads] = e;
         atomicOr(&s_mask[e * W + (t >> 5)], 1u << (t & 31));
@@ -312,7 +318,19 @@ __device__ void bucket_block(const Params &p, int m)
     }
     if (tid == 0) {
         p.offsets[E] = total;
-        const int n1 = ngs * shared_items(p, false) + ngroups * (p.n_rb1 / p.span1) * p.ks1;
+        // gate/up items of span1 row blocks for the routed groups that fit in
+        // the expert kernel's first round of tickets (one item per block);
+        // the groups past them take one row block per item, so that a second
+        // round costs half an item per block instead of a whole one
+        const int per_wide = (p.n_rb1 / p.span1) * p.ks1;
+        int n_wide = ngroups;
+        if (p.span1 > 1) {
+            const int room = p.egrid - ngs * shared_items(p, false);
+            n_wide = min(ngroups, room > 0 ? room / per_wide : 0);
+        }
+        const int n1 = ngs * shared_items(p, false) + n_wide * per_wide +
+                       (ngroups - n_wide) * p.n_rb1 * p.ks1;
+        P->n_wide = n_wide;
         P->m = m;
         P->n_groups = ngroups + ngs;
         P->n_sgroups = ngs;
@@ -329,21 +347,32 @@ __device__ void bucket_block(const Params &p, int m)
 }
 
 // Blocks 0 .. ceil(m / kRouteWaves) - 1: one wave per token does its top-k;
-// the last of these blocks to finish (one counter) buckets the rows. The
-// remaining blocks: one wave per (token, 128-column block) rotates x
-// (codebook) or converts it to fp16 (NVFP4).
+// the last of these blocks to finish (one counter) buckets the rows. With a
+// single top-k block (m <= kRouteWaves = 4) that block buckets right away
+// from the ids it holds in LDS: no counter, no global round trip. (Blocks of
+// 16 waves, one block for 16 tokens, measured slower at m = 16: four top-k
+// waves per SIMD instead of one.) The remaining blocks: one wave per (token, 128-column
+// block) rotates x (codebook) or converts it to fp16 (NVFP4).
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
                                                               const uint16_t *__restrict__ x,
                                                               const float *__restrict__ logits,
                                                               int m)
 {
     __shared__ int s_last;
+    __shared__ int s_ids[kRouteWaves * kMaxTopK];
     const int nk = (m + kRouteWaves - 1) / kRouteWaves;
     const int wave = threadIdx.x >> 6;
+    if (nk == 1 && blockIdx.x == 0) {
+        if (wave < m)
+            route_token(p, logits, wave, s_ids);
+        __syncthreads();
+        bucket_block(p, m, s_ids);
+        return;
+    }
     if ((int)blockIdx.x < nk) {
         const int t = blockIdx.x * kRouteWaves + wave;
         if (t < m)
-            route_token(p, logits, t);
+            route_token(p, logits, t, nullptr);
         wait_stores();
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -354,7 +383,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
         }
         __syncthreads();
         if (s_last)
-            bucket_block(p, m);
+            bucket_block(p, m, nullptr);
         return;
     }
     const int lane = threadIdx.x & 63;
@@ -698,13 +727,31 @@ __device__ __forceinline__ void process_any(const GroupBuf<CLASS> &b, int j, int
 // accumulated into acc. `after(j, buf)` runs once group j is consumed, with
 // the buffer that held it: it loads what that buffer holds next (group j+2 of
 // this chunk, or one of the first two groups of the next chunk or item).
+// Wave priority (wave-uniform p, 0..3). The issue arbiter picks the highest
+// priority first and the oldest wave among equals.
+__device__ __forceinline__ void set_prio(int p)
+{
+    switch (p & 3) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+    }
+}
+
+// Groups 0..NG-1 of a row block. Before group j the wave takes priority
+// (rot + j) mod 4, rot = the block's residency slot on its CU: the four blocks
+// of a CU hold a rotating permutation of the levels, so each runs a quarter of
+// its groups at each level instead of the oldest block always going first.
 template <int CLASS, int NG, typename After>
 __device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
                                               const _Float16 *Arow, const uint32_t (&tab)[4],
-                                              uint32_t lbase, floatx4 (&acc)[kWaveRB], After &after)
+                                              uint32_t lbase, floatx4 (&acc)[kWaveRB], After &after,
+                                              int rot)
 {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
+        set_prio(rot + j);
         GroupBuf<CLASS> &b = (j & 1) ? bB : bA;
         process_any<CLASS>(b, j, bits, Arow, tab, lbase, acc);
         after(j, b);
@@ -736,8 +783,10 @@ struct GroupLds {
 // Ticket t of a phase (gate/up, then down) maps to a row group, a row block
 // and a column split; the shared expert's groups come first. Where its items
 // cover half row blocks (6-bit codes), a row block has two halves per split.
+// Gate/up items of the first n_wide routed groups cover span1 row blocks, the
+// later groups' items one.
 __device__ __forceinline__ Item make_item(const Params &p, int n_items, int n_items1, int n_sg,
-                                          const GroupLds &gl, int ticket)
+                                          int n_wide, const GroupLds &gl, int ticket)
 {
     Item it{};
     it.valid = ticket < n_items;
@@ -759,12 +808,19 @@ __device__ __forceinline__ Item make_item(const Params &p, int n_items, int n_it
             it.half = rbh & 1;
     } else {
         t -= n_sg * per_s;
+        int u0 = n_sg;
         it.span = it.down ? 1 : p.span1;
-        const int per_u = (it.down ? p.n_rb2 : p.n_rb1 / p.span1) * ks;
+        if (!it.down && t >= n_wide * (p.n_rb1 / p.span1) * ks) {
+            // past the wide groups: one row block per item
+            t -= n_wide * (p.n_rb1 / p.span1) * ks;
+            u0 += n_wide;
+            it.span = 1;
+        }
+        const int per_u = (it.down ? p.n_rb2 : p.n_rb1 / it.span) * ks;
         const int v = t / per_u;
         const int rem = t - v * per_u;
         const int rbs = rem / ks;
-        it.u = n_sg + v;
+        it.u = u0 + v;
         it.rb = rbs * it.span;
         it.kq = rem - rbs * ks;
     }
@@ -1080,11 +1136,13 @@ void expert_kernel(Params p)
     // 6-bit codebook slot: the waves of one gate/up half (same tensor in every item)
     const uint32_t lut_slot = (uint32_t)(wave / (kExpertWaves / kLut6Slots));
     const int m = uniform(P->m), n_items = uniform(P->n_items), n_items1 = uniform(P->n_items1);
-    const int n_groups = uniform(P->n_groups), n_sg = uniform(P->n_sgroups);
+    const int n_sg = uniform(P->n_sgroups), n_wide = uniform(P->n_wide);
 
     int *s_tab = (int *)((char *)Abuf + p.lds_tab);
     const GroupLds s_grp{s_tab, s_tab + p.gcap, s_tab + 2 * p.gcap};
-    for (int i = tid; i < n_groups; i += kExpertThreads) {
+    // all p.gcap entries (the run's bound; entries past its groups are never
+    // read): the loads need not wait for the plan's group count
+    for (int i = tid; i < p.gcap; i += kExpertThreads) {
         s_tab[i] = P->g_expert[i];
         s_tab[p.gcap + i] = P->g_off[i];
         s_tab[2 * p.gcap + i] = P->g_rows[i];
@@ -1092,7 +1150,10 @@ void expert_kernel(Params p)
     __syncthreads();
 
     int ticket = blockIdx.x;
-    Item cur = make_item(p, n_items, n_items1, n_sg, s_grp, ticket);
+    // residency slot: blocks b, b + C, b + 2C, ... (C = grid / blocks per CU)
+    // share a CU, dispatched in that order
+    const int rot = uniform((int)(blockIdx.x / max(1u, gridDim.x / 4u)));
+    Item cur = make_item(p, n_items, n_items1, n_sg, n_wide, s_grp, ticket);
     int tok = load_token(p, cur, m, r16);
     uint32_t done = 0;
     if (cur.valid) {
@@ -1109,7 +1170,8 @@ void expert_kernel(Params p)
             // after the item's last row block comes the next item: its plan
             // entries (LDS) and descriptor (vector loads)
             const int nxt_ticket = ticket + (int)gridDim.x;
-            const Item nxt = make_item(p, n_items, n_items1, n_sg, s_grp, last ? nxt_ticket : n_items);
+            const Item nxt = make_item(p, n_items, n_items1, n_sg, n_wide, s_grp,
+                                       last ? nxt_ticket : n_items);
             const DescRaw dn = load_desc(p, nxt, wave);
             const int tok_n = load_token(p, nxt, m, r16);
 
@@ -1163,7 +1225,7 @@ void expert_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < kWaveRB; ++i)
                 acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, lut_slot * 128u, acc, after);
+            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, lut_slot * 128u, acc, after, rot);
             if constexpr (!is_cb<CLASS>)
 #pragma unroll
                 for (int i = 0; i < kWaveRB; ++i)

@@ -333,6 +333,7 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
     p.span1 = h->span1[m];
     p.gcap = h->gcap[m];
     p.lds_tab = h->lds_tab[m];
+    p.egrid = h->grid[m];
     const bool pf = h->prefill[m] != 0;
     p.group_rows = pf ? kPrefillRows : kGroupRows;
     HIP_TRY(launch_route(p, (const uint16_t *)x_bf16, logits, m, s));

@@ -44,7 +44,9 @@ struct Plan {
     int32_t n_items1;      // gate/up work items
     int32_t n_items;       // all work items
     int32_t n_sgroups;     // row groups of the shared expert (groups 0 .. n_sgroups-1)
-    int32_t pad[3];
+    int32_t n_wide;        // routed groups whose gate/up items span span1 row blocks;
+                           // the routed groups after them take one row block per item
+    int32_t pad[2];
     int32_t g_expert[kMaxGroups];  // expert of group u (groups in expert order)
     int32_t g_off[kMaxGroups];     // first row of u in the bucket row list
     int32_t g_rows[kMaxGroups];    // rows of u (1..group_rows)
@@ -77,6 +79,7 @@ struct Params {
                            // 6-bit codes make a full row block three 2-bit ones)
     int32_t group_rows;    // rows per row group: 16 (persistent decode kernel) or 64 (prefill)
     int32_t gcap;          // row-group table entries in LDS (bound on the groups of a run)
+    int32_t egrid;         // expert-kernel blocks of the run (set per run)
     int32_t lds_tab;       // byte offset of that table in the expert kernel's dynamic LDS
     uint32_t spin_limit;   // polls before a dependency wait gives up
     float *out;            // [m][H] result of the current launch
