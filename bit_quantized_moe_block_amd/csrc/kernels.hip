@@ -739,19 +739,20 @@ __device__ __forceinline__ void set_prio(int p)
     }
 }
 
-// Groups 0..NG-1 of a row block. Before group j the wave takes priority
-// (rot + j) mod 4, rot = the block's residency slot on its CU: the four blocks
-// of a CU hold a rotating permutation of the levels, so each runs a quarter of
-// its groups at each level instead of the oldest block always going first.
+// Groups 0..NG-1 of a row block. Gate/up items (their h is what down items
+// wait for) run above down items: before group j a gate/up wave takes
+// priority 1 + (rot + j) mod 3, rot = the block's residency slot on its CU,
+// so the gate/up blocks of a CU rotate through the levels instead of the
+// oldest always going first; down items take priority 0.
 template <int CLASS, int NG, typename After>
 __device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
                                               const _Float16 *Arow, const uint32_t (&tab)[4],
                                               uint32_t lbase, floatx4 (&acc)[kWaveRB], After &after,
-                                              int rot)
+                                              int rot, bool down)
 {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-        set_prio(rot + j);
+        set_prio(down ? 0 : 1 + (rot + j) % 3);
         GroupBuf<CLASS> &b = (j & 1) ? bB : bA;
         process_any<CLASS>(b, j, bits, Arow, tab, lbase, acc);
         after(j, b);
@@ -1071,6 +1072,7 @@ __device__ __forceinline__ void complete_item(const Params &p, const Item &it, S
     const int tid = threadIdx.x;
     if (it.down)
         return;
+    __builtin_amdgcn_s_setprio(3);  // finishing h is on the down items' path
     wait_stores();
     __syncthreads();
     // a row block's arrivals: one per column split, or two (one per half)
@@ -1152,7 +1154,7 @@ void expert_kernel(Params p)
     int ticket = blockIdx.x;
     // residency slot: blocks b, b + C, b + 2C, ... (C = grid / blocks per CU)
     // share a CU, dispatched in that order
-    const int rot = uniform((int)(blockIdx.x / max(1u, gridDim.x / 4u)));
+    const int rot = uniform((int)(blockIdx.x / max(1u, gridDim.x / 4u))) % 3;
     Item cur = make_item(p, n_items, n_items1, n_sg, n_wide, s_grp, ticket);
     int tok = load_token(p, cur, m, r16);
     uint32_t done = 0;
@@ -1225,7 +1227,8 @@ void expert_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < kWaveRB; ++i)
                 acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, lut_slot * 128u, acc, after, rot);
+            compute_chunk<CLASS, NG>(bA, bB, J.bits, Arow, tab, lut_slot * 128u, acc, after, rot,
+                                     cur.down != 0);
             if constexpr (!is_cb<CLASS>)
 #pragma unroll
                 for (int i = 0; i < kWaveRB; ++i)
