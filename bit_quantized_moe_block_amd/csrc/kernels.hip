@@ -1183,6 +1183,8 @@ void expert_kernel(Params p)
                 // items: once thread 0 has seen the group's h complete, a
                 // bounded wait) its activation rows: the weights do not
                 // depend on h and load during the wait
+                // the item's loads leave first, at the top priority
+                __builtin_amdgcn_s_setprio(3);
                 u32x4 lut = u32x4{0, 0, 0, 0};
                 _Float16 lut6 = 0;
                 if constexpr (is_cb<CLASS>) {
@@ -1194,6 +1196,7 @@ void expert_kernel(Params p)
                 if constexpr (NG > 1)
                     load_group<CLASS, 0>(bB, J, 1, lane, sc_lane);
                 if (cur.down) {
+                    __builtin_amdgcn_s_setprio(0);  // waiting yields to the others
                     if (tid == 0)
                         sm.flag = wait_h(p, cur.u);
                     __syncthreads();
