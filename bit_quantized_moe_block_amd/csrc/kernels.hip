@@ -856,14 +856,17 @@ __device__ __forceinline__ DescRaw load_desc(const Params &p, const Item &it, in
     return d;
 }
 
-// Token of bucket row min(r16, R-1) of a gate/up item's group, for lane r16:
-// routed rows from the row list, the shared expert's row m*k + t is token t.
-// Loaded one item ahead, with the item's descriptor.
+// For lane r16, bucket row q = off + min(r16, R-1) of the item's group: a
+// gate/up item's token of q, a down item's pair index of q (t*k + j for a
+// routed row, q itself for the shared expert's row m*k + t), under which its
+// partial sums are stored. Loaded one item ahead, with the item's descriptor.
 __device__ __forceinline__ int load_token(const Params &p, const Item &it, int m, int r16)
 {
-    if (!it.valid || it.down)
+    if (!it.valid)
         return 0;
     const int q = it.off + min(r16, it.R - 1);
+    if (it.down)
+        return q < m * p.k ? p.rows[q] : q;
     return q < m * p.k ? p.rows[q] / p.k : q - m * p.k;
 }
 
@@ -1036,9 +1039,12 @@ struct Stage {
 // Store the partial sums of one row block of an item (rows rb0.. of job J).
 // Gate/up partials go out agent-coherent for the finishing block; down
 // partials are read only by the combine kernel, after this kernel ends.
+// Results of an item: gate/up partials under the bucket row, down partials
+// under the row's pair index (tok: see load_token), so that the combine reads
+// them without the bucket positions.
 template <int CLASS>
 __device__ __forceinline__ void store_rows(const Params &p, const Item &it, const WaveJob &J,
-                                           const floatx4 (&acc)[kWaveRB])
+                                           const floatx4 (&acc)[kWaveRB], int tok)
 {
     const int tid = threadIdx.x;
     // the lane index, opaque to the compiler: the addresses below are
@@ -1048,13 +1054,17 @@ __device__ __forceinline__ void store_rows(const Params &p, const Item &it, cons
     asm volatile("" : "+v"(lane));
     const int proj = item_proj(it, tid >> 6);
     const int ntiles = has6<CLASS> && J.bits == 6 ? kWaveRB / 2 : kWaveRB;  // 6-bit: 2 per wave
+    int pr[4];  // down: pair index of row 4 (lane / 16) + j, from the lane holding it
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        pr[j] = __shfl(tok, 4 * (lane >> 4) + j);
 #pragma unroll
     for (int i = 0; i < kWaveRB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int tok = 4 * (lane >> 4) + j;
-            if (i < ntiles && tok < it.R) {
-                const size_t row = (size_t)it.kq * p.pair_cap + it.off + tok;
+            const int r = 4 * (lane >> 4) + j;
+            if (i < ntiles && r < it.R) {
+                const size_t row = (size_t)it.kq * p.pair_cap + (it.down ? pr[j] : it.off + r);
                 const int n = (J.rb0 + i) * 16 + (lane & 15);
                 if (it.down)
                     p.y_part[row * p.H + n] = acc[i][j];
@@ -1237,7 +1247,7 @@ void expert_kernel(Params p)
                 for (int i = 0; i < kWaveRB; ++i)
                     acc[i] *= J.ts;
             if (ok)
-                store_rows<CLASS>(p, cur, J, acc);
+                store_rows<CLASS>(p, cur, J, acc, tok);
             if (!last) {
                 ++sb;
                 J = JN;
@@ -1264,7 +1274,7 @@ void expert_kernel(Params p)
 // Combine
 // ---------------------------------------------------------------------------
 
-// out[t][n] = sum_j w[t][j] * sum_s y_part[s][pos(t, j)][n], slots j in
+// out[t][n] = sum_j w[t][j] * sum_s y_part[s][t*k + j][n], slots j in
 // order, splits s in order (no float atomics: bitwise reproducible), plus
 // the shared expert's row (weight 1) when there is one. Block
 // (rb, t) covers rows rb*256 .. +255 of token t; runs after the expert
@@ -1282,7 +1292,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p)
             pp[jj] = 0;
             wj[jj] = 0.0f;
             if (j0 + jj < p.k) {
-                pp[jj] = p.pos[t * p.k + j0 + jj];
+                pp[jj] = t * p.k + j0 + jj;  // partials are stored by pair index
                 wj[jj] = p.wts[t * p.k + j0 + jj];
             }
         }
@@ -1495,7 +1505,18 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     // result layout: lane holds rows 16t + 4q + j (j = 0..3) of subtile t,
     // output row 16i + r16 of the wave's tile i
     if constexpr (DOWN) {
+        // y goes out under each row's pair index (t*k + j for a routed row,
+        // the bucket row itself for the shared expert's), as the combine reads it
         const int n0 = rb * 256 + wave * (kPfNT * 16);
+        const int mk = uniform(p.plan->m) * p.k;
+        int pair[NSUB][4];
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int qr = off + min(16 * t + 4 * q + j, R - 1);
+                pair[t][j] = qr < mk ? p.rows[qr] : qr;
+            }
 #pragma unroll
         for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
@@ -1504,7 +1525,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * t + 4 * q + j;
                     if (row < R)
-                        p.y_part[(size_t)(off + row) * p.H + n0 + 16 * i + r16] = acc[i][t][j];
+                        p.y_part[(size_t)pair[t][j] * p.H + n0 + 16 * i + r16] = acc[i][t][j];
                 }
     } else {
         // h = silu(g) u through LDS (the up waves' u, then the gate waves'
