@@ -98,6 +98,42 @@ def test_full_layer_sampled(full_layer, m):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("m", [16, 24])
+def test_full_layer_one_row_block_items(full_layer, m):
+    # From m = 8 gate/up items span two row blocks, but only for the row
+    # groups that fit in the first round of tickets (one item per resident
+    # block); the later groups take one-row-block items. 34 (m = 16) and 41
+    # (m = 24) row groups overflow the 32 that fit: the run's item count must
+    # be that of the mixed layout, and tokens routed into the one-row-block
+    # groups must match the oracle.
+    d, layer = full_layer
+    w = d["workload"]
+    case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
+    say(f"[parity] full_layer one-row-block items m={m}")
+    out = run_gpu(layer, case)
+    info, st = layer.info(), layer.stats()
+    assert st.error_word == 0 and st.items_done == st.items
+    rid, _ = oracle.route(case["logits"], w.top_k)
+    b = oracle.bucket(rid, w.num_experts)
+    groups = [(e, g) for e in range(w.num_experts) for g in range((int(b["counts"][e]) + 15) // 16)]
+    n_rb1, n_rb2 = w.inter // 128, w.hidden // 256
+    ks1, ks2 = info.k_split_gate_up, info.k_split_down
+    per_wide = (n_rb1 // 2) * ks1
+    n_wide = min(len(groups), info.grid_blocks // per_wide)
+    assert n_wide < len(groups), "the layer must overflow the first round"
+    assert st.items == (n_wide * per_wide + (len(groups) - n_wide) * n_rb1 * ks1
+                        + len(groups) * n_rb2 * ks2)
+    late = set()
+    for e, g in groups[n_wide:]:
+        lo = int(b["offsets"][e]) + 16 * g
+        late.update(int(t) for t in b["rows_t"][lo:min(lo + 16, int(b["offsets"][e + 1]))])
+    tokens = sorted(late)[:: max(1, len(late) // 3)][:3]
+    ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
+    err = rel_err(out, ref["out"], tokens)
+    say(f"    groups={len(groups)} wide={n_wide} items={st.items} tokens={tokens} rel={err:.3e}")
+    assert err <= REL_TOL
+
+
 @pytest.mark.parametrize("layer", [3, 20, 43])
 def test_pack_layers_sampled(layer):
     # The pack mix at full size and the 16-row batch: an all-2-bit routed layer,
