@@ -1338,9 +1338,9 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p)
 // Prefill / batched verify (more than 32 tokens): grouped GEMM over buckets
 // ---------------------------------------------------------------------------
 // With many tokens an expert has tens to hundreds of rows. The buckets are
-// cut into row groups of up to 64 rows, and each decoded weight step feeds the
-// MFMAs of all four 16-row subtiles of the group: the decode, the VALU cost
-// of these formats, is paid once per 64 rows instead of once per 16. A block
+// cut into row groups of up to 64 rows, and each decoded weight step feeds
+// one MFMA per 16-row subtile of the group (up to four): the decode, the VALU
+// cost of these formats, is paid once per 64 rows instead of once per 16. A block
 // covers one row group and 128 output rows (of gate and of up: four waves
 // each) or 256 (down), over all input columns, so there are no column splits
 // and no partial sums. The gate/up block finishes SiLU(g) u and the h
@@ -1394,12 +1394,13 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t w, _Float16 f)
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, w) * half2v{f, f});
 }
 
-// One 128-column group of the wave's kPfNT tiles against the four staged
-// 16-row subtiles (A, B and result layouts as in process_group; subtile t =
-// rows 16t .. 16t+15). Per step: the subtiles' A operands, then per tile one
-// decode and four MFMAs. A group with fewer rows still runs all four: its
-// staged rows past R repeat row R-1 and their results are never stored, and
-// per-subtile branches cost more issue slots than the MFMAs they skip. The
+// One 128-column group of the wave's kPfNT tiles against the first NSUB
+// staged 16-row subtiles (A, B and result layouts as in process_group;
+// subtile t = rows 16t .. 16t+15; NSUB = ceil(R / 16), fixed per loop
+// instance: per-subtile branches inside the loop cost more issue slots than
+// the MFMAs they skip). Per step: the subtiles' A operands, then per tile one
+// decode and NSUB MFMAs; staged rows past R repeat row R-1 and their results
+// are never stored. The
 // decoded weights carry the group scale already (fp16 entry x scale, one more
 // fp16 rounding, as the NVFP4 block scale), so the accumulators take the
 // products directly: per-group partial results for every (tile, subtile)
