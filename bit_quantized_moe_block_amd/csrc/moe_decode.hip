@@ -90,11 +90,11 @@ static int group_cap(const Params &p, int m, int rows = kGroupRows)
 
 // From this many tokens on the prefill kernels run (64-row groups, one decode
 // per 64 rows), unless a tensor has 6-bit codes (the persistent kernel serves
-// those at every m). Below it the persistent kernel is as fast or faster:
-// measured on the 4096 x 2048 layer with Zipf routing, per layer, persistent
-// vs prefill: m = 64 249 vs 277 us, 128 370 vs 371, 256 570 vs 483, 512 959
-// vs 686.
-constexpr int kPrefillFrom = 128;
+// those at every m). Below it the persistent kernel is faster: measured on the
+// 4096 x 2048 layer with Zipf routing, per layer, persistent vs prefill:
+// m = 16 103 vs 114 us, 24 148 vs 161, 32 161 vs 169, 48 193 vs 184,
+// 64 227 vs 212, 96 293 vs 251.
+constexpr int kPrefillFrom = 48;
 
 static moe_status validate(const moe_decode_config *c)
 {

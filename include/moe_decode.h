@@ -143,7 +143,7 @@ moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
  * returns MOE_E_STREAM (page "LNA-CANON.md", "lna2 とは": concurrent streams
  * are forbidden; page "lna-lab/README.md", "The three traps", item 3: two
  * streams sharing one lock buffer deadlocked). Results are bitwise identical
- * for identical inputs (same m). From m = 128 on (without 6-bit tensors) the
+ * for identical inputs (same m). From m = 48 on (without 6-bit tensors) the
  * step runs grouped-GEMM prefill kernels instead of the persistent decode
  * kernel (page "LNA-CANON.md", section "起動": prefill batches of up to 512
  * tokens); a token's output then differs from a run at smaller m in rounding
