@@ -1357,18 +1357,26 @@ constexpr int kPfAStride = 128 + kLdsPadHalves;   // staged chunk row stride (ha
 constexpr int kPfHStride = 128 + 4;               // epilogue buffer row stride (floats)
 constexpr size_t kPfLds = 2 * kPfRows * kPfAStride * sizeof(_Float16);
 
-// One 128-column chunk of the group's activation rows: 64 rows x 128 fp16 =
-// 1024 16-byte pieces, two per thread; rows past R repeat row R-1 (their
-// results are never stored). Gate/up rows are tokens: lane r of every wave
-// holds the token of row r. Down rows off .. off+R-1 of h~ are consecutive.
+// One 128-column chunk of the first ROWS activation rows of the group (the
+// rows of its NSUB subtiles, ROWS = 16 NSUB): ROWS x 128 fp16 = 16 ROWS
+// 16-byte pieces, piece i by thread i mod 512; rows past R repeat row R-1
+// (their results are never stored). A piece index past the end skips whole
+// waves (256 pieces = 4 waves). Gate/up rows are tokens: lane r of every
+// wave holds the token of row r. Down rows off .. off+R-1 of h~ are
+// consecutive.
+template <int ROWS>
 struct PfStage {
-    u32x4 v[2];
+    static constexpr int PIECES = ROWS * 16;
+    static constexpr int ITERS = (PIECES + kPfThreads - 1) / kPfThreads;
+    u32x4 v[ITERS];
     __device__ __forceinline__ void issue(const Params &p, bool down, int off, int R, int tok, int c)
     {
         const int tid = threadIdx.x;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < ITERS; ++k) {
             const int i = tid + k * kPfThreads;
+            if (PIECES % kPfThreads != 0 && i >= PIECES)
+                continue;
             const int row = min(i >> 4, R - 1), col = c * 128 + (i & 15) * 8;
             const _Float16 *src = down ? p.hr + (size_t)(off + row) * p.I + col
                                        : p.xr + (size_t)__shfl(tok, row) * p.H + col;
@@ -1379,8 +1387,10 @@ struct PfStage {
     {
         const int tid = threadIdx.x;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < ITERS; ++k) {
             const int i = tid + k * kPfThreads;
+            if (PIECES % kPfThreads != 0 && i >= PIECES)
+                continue;
             *(u32x4 *)(A + (i >> 4) * kPfAStride + (i & 15) * 8) = v[k];
         }
     }
@@ -1465,7 +1475,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     // old value, and the register copies that merge takes wait for every
     // load in flight
     GroupBuf<CLASS, kPfNT> bA, bB;
-    PfStage st;
+    PfStage<16 * NSUB> st;
     const int G1 = J.G - 1;
     st.issue(p, DOWN, off, R, tok, 0);
     load_group<CLASS, KB, kPfNT>(bA, J, 0, lane, sc_lane);
