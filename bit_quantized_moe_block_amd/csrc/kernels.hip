@@ -1363,23 +1363,33 @@ constexpr size_t kPfLds = 2 * kPfRows * kPfAStride * sizeof(_Float16);
 // (their results are never stored). A piece index past the end skips whole
 // waves (256 pieces = 4 waves). Gate/up rows are tokens: lane r of every
 // wave holds the token of row r. Down rows off .. off+R-1 of h~ are
-// consecutive.
+// consecutive. A thread's rows are the same in every chunk: their element
+// offsets (row x row length, below 2^31) are computed once.
 template <int ROWS>
 struct PfStage {
     static constexpr int PIECES = ROWS * 16;
     static constexpr int ITERS = (PIECES + kPfThreads - 1) / kPfThreads;
     u32x4 v[ITERS];
-    __device__ __forceinline__ void issue(const Params &p, bool down, int off, int R, int tok, int c)
+    int rowoff[ITERS];
+    __device__ __forceinline__ void init(const Params &p, bool down, int off, int R, int tok)
     {
         const int tid = threadIdx.x;
+#pragma unroll
+        for (int k = 0; k < ITERS; ++k) {
+            const int row = min((tid + k * kPfThreads) >> 4, R - 1);
+            rowoff[k] = down ? (off + row) * p.I : __shfl(tok, row) * p.H;
+        }
+    }
+    __device__ __forceinline__ void issue(const Params &p, bool down, int c)
+    {
+        const int tid = threadIdx.x;
+        const _Float16 *base = down ? p.hr : p.xr;
 #pragma unroll
         for (int k = 0; k < ITERS; ++k) {
             const int i = tid + k * kPfThreads;
             if (PIECES % kPfThreads != 0 && i >= PIECES)
                 continue;
-            const int row = min(i >> 4, R - 1), col = c * 128 + (i & 15) * 8;
-            const _Float16 *src = down ? p.hr + (size_t)(off + row) * p.I + col
-                                       : p.xr + (size_t)__shfl(tok, row) * p.H + col;
+            const _Float16 *src = base + rowoff[k] + c * 128 + (i & 15) * 8;
             v[k] = *(const u32x4 GLOBAL *)src;
         }
     }
@@ -1477,7 +1487,8 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     GroupBuf<CLASS, kPfNT> bA, bB;
     PfStage<16 * NSUB> st;
     const int G1 = J.G - 1;
-    st.issue(p, DOWN, off, R, tok, 0);
+    st.init(p, DOWN, off, R, tok);
+    st.issue(p, DOWN, 0);
     load_group<CLASS, KB, kPfNT>(bA, J, 0, lane, sc_lane);
     st.commit(pf_lds);
     load_group<CLASS, KB, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
@@ -1495,7 +1506,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     auto step = [&](int c, GroupBuf<CLASS, kPfNT> &b) {
         const _Float16 *A = (c & 1) ? half1 : half0;
         _Float16 *Anext = (c & 1) ? half0 : half1;
-        st.issue(p, DOWN, off, R, tok, min(c + 1, G1));
+        st.issue(p, DOWN, min(c + 1, G1));
         if (c < J.G)
             pf_group<CLASS, FMT, NSUB>(b, A, lut, acc);
         load_group<CLASS, KB, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
