@@ -1279,11 +1279,13 @@ void expert_kernel(Params p)
 // the shared expert's row (weight 1) when there is one. Block
 // (rb, t) covers rows rb*256 .. +255 of token t; runs after the expert
 // kernel, so plain loads see its partial sums.
-__global__ __launch_bounds__(256) void combine_kernel(Params p)
+__global__ __launch_bounds__(64) void combine_kernel(Params p)
 {
-    const int t = blockIdx.y, row = blockIdx.x * 256 + threadIdx.x;
+    // one wave per (256-row block, token); lane l owns rows 4l .. 4l+3 of the
+    // block and moves them as 16-byte loads and stores
+    const int t = blockIdx.y, row = blockIdx.x * 256 + 4 * threadIdx.x;
     constexpr int SPP = 4;  // slots per pass
-    float o = 0.0f;
+    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < p.k; j0 += SPP) {
         int pp[SPP];
         float wj[SPP];
@@ -1296,42 +1298,53 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p)
                 wj[jj] = p.wts[t * p.k + j0 + jj];
             }
         }
-        float y[SPP];
+        floatx4 y[SPP];
 #pragma unroll
         for (int jj = 0; jj < SPP; ++jj)
-            y[jj] = 0.0f;
+            y[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < p.ks2; s0 += 2) {
-            float v[SPP][2];
+            floatx4 v[SPP][2];
 #pragma unroll
             for (int jj = 0; jj < SPP; ++jj)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    v[jj][s] = 0.0f;
+                    v[jj][s] = floatx4{0.f, 0.f, 0.f, 0.f};
                     if (j0 + jj < p.k && s0 + s < p.ks2)
-                        v[jj][s] = p.y_part[((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row];
+                        v[jj][s] = *(const floatx4 *)(p.y_part +
+                                                      ((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row);
                 }
 #pragma unroll
             for (int jj = 0; jj < SPP; ++jj)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     if (s0 + s < p.ks2)
-                        y[jj] += v[jj][s];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            y[jj][c] += v[jj][s][c];
         }
 #pragma unroll
         for (int jj = 0; jj < SPP; ++jj)
             if (j0 + jj < p.k)
-                o += wj[jj] * y[jj];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    o[c] += wj[jj] * y[jj][c];
     }
     if (p.has_shared) {
         // the shared expert's row of token t (bucket row m*k + t), weight 1,
         // after the routed slots
         const size_t q = (size_t)gridDim.y * p.k + t;
-        float ysh = 0.0f;
-        for (int s = 0; s < p.ks2; ++s)
-            ysh += p.y_part[((size_t)s * p.pair_cap + q) * p.H + row];
-        o += ysh;
+        floatx4 ysh = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < p.ks2; ++s) {
+            const floatx4 v = *(const floatx4 *)(p.y_part + ((size_t)s * p.pair_cap + q) * p.H + row);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                ysh[c] += v[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            o[c] += ysh[c];
     }
-    p.out[(size_t)t * p.H + row] = o;
+    *(floatx4 *)(p.out + (size_t)t * p.H + row) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -1725,7 +1738,7 @@ hipError_t launch_prefill(const Params &p, int grid_groups, hipStream_t s)
 
 hipError_t launch_combine(const Params &p, int m, hipStream_t s)
 {
-    combine_kernel<<<dim3(p.n_rb2, m), dim3(256), 0, s>>>(p);
+    combine_kernel<<<dim3(p.n_rb2, m), dim3(64), 0, s>>>(p);
     return hipGetLastError();
 }
 
