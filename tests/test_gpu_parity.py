@@ -376,6 +376,11 @@ LARGE_M = [
     (small_workload("lm8", 256, 16, 256, 128, bits_mix="alternate", router="zipf",
                     config_id=409), 512),
     (small_workload("lm9", 32, 16, 256, 128, bits_mix="alternate", config_id=410), 40),
+    # both sides of the switch between the two paths (prefill from 48 tokens)
+    (small_workload("lm10", 32, 8, 512, 256, bits_mix="alternate", router="zipf",
+                    config_id=411), 47),
+    (small_workload("lm11", 32, 8, 512, 256, bits_mix="alternate", router="zipf",
+                    config_id=411), 48),
 ]
 
 
