@@ -9,13 +9,18 @@
 //                The other blocks: one wave per (token, 128-column block)
 //                rotates x (codebook) or converts it to fp16 (NVFP4).
 // expert_kernel  persistent grid, work items assigned round robin (no shared
-//                ticket counter), no grid-wide barrier. Gate/up items (one row group, 128 rows of gate and
-//                of up, one column split) write partial sums; the last split
-//                of a 128-row block finishes SiLU(g)*u and the 128-point
-//                rotation of h. Down items (256 rows of down, one column
-//                split) wait on a per-group counter of finished h blocks; the
-//                last down item touching a (token, 256-row block) combines
-//                that block of the token's output in slot order.
+//                ticket counter), no grid-wide barrier. Gate/up items (one
+//                row group, 128 rows of gate and of up, one column split)
+//                write partial sums; the last split of a 128-row block
+//                finishes SiLU(g)*u and the 128-point rotation of h. Down
+//                items (256 rows of down, one column split) wait on a
+//                per-group counter of finished h blocks and store their
+//                partial sums under the pair index.
+// combine_kernel one wave per (token, 256-row block): the down partial sums
+//                of the token's k slots, in slot order, times the router
+//                weights (NaN if the expert kernel reported an error).
+// prefill_kernel from 48 tokens on: grouped GEMM over 64-row groups, gate/up
+//                then down as two launches.
 //                Inner loop: codes decoded in registers (v_perm byte lookups
 //                of the per-tensor codebook, or hardware e2m1 conversion),
 //                MFMA 16x16x32 f16 with the tokens as the A operand, fp32
@@ -1344,6 +1349,11 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p)
         for (int c = 0; c < 4; ++c)
             o[c] += ysh[c];
     }
+    // a dependency wait of the expert kernel gave up (some down partial
+    // sums are stale): the failure shows in the output instead of a
+    // plausible wrong value
+    if (__builtin_amdgcn_readfirstlane(*(volatile uint32_t *)&p.ctr->error_word) != 0u)
+        o = floatx4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     *(floatx4 *)(p.out + (size_t)t * p.H + row) = o;
 }
 

@@ -41,6 +41,7 @@ struct moe_decode_s {
     bool ran = false;
     int last_m = 0;
     bool last_prefill = false;
+    Params last{};               // parameters of the last run (its buffers: queries read them)
     hipEvent_t ev_begin = nullptr, ev_end = nullptr;
 };
 
@@ -96,6 +97,62 @@ static int group_cap(const Params &p, int m, int rows = kGroupRows)
 // 64 227 vs 212, 96 293 vs 251.
 constexpr int kPrefillFrom = 48;
 
+// Byte offsets of the per-run buffers in one scratch block, for runs of up to
+// `tokens` tokens with `pc` bucket rows and `gmax` row groups (256-byte
+// aligned pieces). The counters come first: handles of different shapes that
+// share one block (the static scratch below) find them at the same place.
+struct Layout {
+    size_t ctr, rbdone, hready, ids, wts, counts, offsets, rows, pos, plan, xr, gu, hr, y, end;
+};
+
+static Layout scratch_layout(const Params &p, size_t tokens, size_t pc, size_t gmax)
+{
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) & ~size_t(255);
+        return o;
+    };
+    const size_t E = p.E, H = p.H, I = p.I;
+    const size_t ctr_b = 4 * kCtrStride;  // one counter per 128-byte line
+    L.ctr = take(sizeof(Counters));
+    L.rbdone = take(ctr_b * gmax * p.n_rb1);
+    L.hready = take(ctr_b * gmax);
+    L.ids = take(4 * pc);
+    L.wts = take(4 * pc);
+    L.counts = take(4 * E);
+    L.offsets = take(4 * (E + 1));
+    L.rows = take(4 * pc);
+    L.pos = take(4 * pc);
+    L.plan = take(sizeof(Plan));
+    L.xr = take(2 * tokens * H);
+    L.gu = take(4 * (size_t)p.ks1 * pc * 2 * I);
+    L.hr = take(2 * pc * I);
+    L.y = take(4 * (size_t)p.ks2 * pc * H);
+    L.end = off;
+    return L;
+}
+
+// Point the per-run buffers of p into the block at `base` laid out by L.
+static void bind_scratch(Params &p, char *base, const Layout &L)
+{
+    p.ctr = (Counters *)(base + L.ctr);
+    p.rb_done = (uint32_t *)(base + L.rbdone);
+    p.h_ready = (uint32_t *)(base + L.hready);
+    p.ids = (int32_t *)(base + L.ids);
+    p.wts = (float *)(base + L.wts);
+    p.counts = (int32_t *)(base + L.counts);
+    p.offsets = (int32_t *)(base + L.offsets);
+    p.rows = (int32_t *)(base + L.rows);
+    p.pos = (int32_t *)(base + L.pos);
+    p.plan = (Plan *)(base + L.plan);
+    p.xr = (_Float16 *)(base + L.xr);
+    p.gu_part = (float *)(base + L.gu);
+    p.hr = (_Float16 *)(base + L.hr);
+    p.y_part = (float *)(base + L.y);
+}
+
 static moe_status validate(const moe_decode_config *c)
 {
     if (!c)
@@ -145,6 +202,11 @@ static moe_status validate(const moe_decode_config *c)
                 if (t.bits != 2 && t.bits != 3 && t.bits != 6)
                     return fail(MOE_E_INVALID, "expert %d projection %d: bits %d not 2, 3 or 6", e,
                                 p, t.bits);
+                // 6-bit codes are the stored form of the shared expert only (the
+                // pack's dense linears); routed experts are 2/3-bit
+                if (t.bits == 6 && e < c->num_experts)
+                    return fail(MOE_E_UNSUPPORTED,
+                                "expert %d: 6-bit codes are supported for the shared expert only", e);
                 if (!t.lut)
                     return fail(MOE_E_INVALID, "expert %d projection %d: NULL lut", e, p);
                 if (!aligned(t.codes, 16) || !aligned(t.scales, 16) || !aligned(t.lut, 4))
@@ -196,6 +258,12 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     p.sh_half = cfg->shared && cfg->shared[0].bits == 6;
     p.pair_cap = p.max_tokens * (p.k + p.has_shared);
     p.spin_limit = 2u * 1000u * 1000u;  // polls of up to ~1 us: a ~2 s bound
+    // Test hook: MOE_DECODE_SPIN_LIMIT=<polls> shortens the bound of the
+    // dependency waits, so that a test can make them give up (every kernel
+    // still ends normally; the failure then shows as MOE_E_DEVICE and NaN
+    // outputs). It changes no result of a run that completes.
+    if (const char *sl = getenv("MOE_DECODE_SPIN_LIMIT"))
+        p.spin_limit = (uint32_t)strtoul(sl, nullptr, 10);
     p.signs_h = cfg->signs_hidden;
     p.signs_i = cfg->signs_inter;
     h->max_tokens = cfg->max_tokens;
@@ -215,46 +283,20 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
         return cleanup(fail(MOE_E_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(err)));
     h->cu_count = prop.multiProcessorCount;
 
-    // Scratch layout (256-byte aligned pieces).
-    const size_t E = p.E, PC = p.pair_cap, H = p.H, I = p.I, M = p.max_tokens;
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        size_t o = off;
-        off += (bytes + 255) & ~size_t(255);
-        return o;
-    };
-    const size_t o_tensors = take(sizeof(DevTensor) * (E * 3 + 3));
-    const size_t o_ids = take(4 * PC), o_wts = take(4 * PC), o_counts = take(4 * E),
-                 o_offsets = take(4 * (E + 1)), o_rows = take(4 * PC), o_pos = take(4 * PC);
-    const size_t o_plan = take(sizeof(Plan));
-    const size_t ctr_b = 4 * kCtrStride;  // one counter per 128-byte line
-    const size_t gmax = group_cap(p, p.max_tokens);
-    const size_t o_ctr = take(sizeof(Counters)), o_rbdone = take(ctr_b * gmax * p.n_rb1),
-                 o_hready = take(ctr_b * gmax);
-    const size_t ctr_end = off;
-    const size_t o_xr = take(2 * M * H), o_gu = take(4 * (size_t)p.ks1 * PC * 2 * I),
-                 o_hr = take(2 * PC * I), o_y = take(4 * (size_t)p.ks2 * PC * H);
-    h->scratch_bytes = off;
-    err = hipMalloc(&h->scratch, off);
+    // The handle's scratch: the per-run buffers for max_tokens, then the
+    // device copy of the descriptor table.
+    const size_t E = p.E, M = p.max_tokens;
+    const Layout L = scratch_layout(p, M, p.pair_cap, group_cap(p, p.max_tokens));
+    const size_t o_tensors = L.end;
+    const size_t total = o_tensors + sizeof(DevTensor) * (E * 3 + 3);
+    h->scratch_bytes = total;
+    err = hipMalloc(&h->scratch, total);
     if (err != hipSuccess)
-        return cleanup(fail(MOE_E_NOMEM, "hipMalloc(%zu) failed: %s", off, hipGetErrorString(err)));
+        return cleanup(fail(MOE_E_NOMEM, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(err)));
     char *base = (char *)h->scratch;
     h->dev_tensors = (DevTensor *)(base + o_tensors);
     p.tensors = h->dev_tensors;
-    p.ids = (int32_t *)(base + o_ids);
-    p.wts = (float *)(base + o_wts);
-    p.counts = (int32_t *)(base + o_counts);
-    p.offsets = (int32_t *)(base + o_offsets);
-    p.rows = (int32_t *)(base + o_rows);
-    p.pos = (int32_t *)(base + o_pos);
-    p.plan = (Plan *)(base + o_plan);
-    p.ctr = (Counters *)(base + o_ctr);
-    p.rb_done = (uint32_t *)(base + o_rbdone);
-    p.h_ready = (uint32_t *)(base + o_hready);
-    p.xr = (_Float16 *)(base + o_xr);
-    p.gu_part = (float *)(base + o_gu);
-    p.hr = (_Float16 *)(base + o_hr);
-    p.y_part = (float *)(base + o_y);
+    bind_scratch(p, base, L);
 
     std::vector<DevTensor> tab(E * 3 + 3, DevTensor{});
     for (size_t i = 0; i < E * 3 + (cfg->shared ? 3 : 0); ++i) {
@@ -263,8 +305,8 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     }
     err = hipMemcpy(h->dev_tensors, tab.data(), sizeof(DevTensor) * (E * 3 + 3),
                     hipMemcpyHostToDevice);
-    if (err == hipSuccess)
-        err = hipMemset(base + o_ids, 0, ctr_end - o_ids);
+    if (err == hipSuccess)  // counters (rb_done and h_ready are reset by every run)
+        err = hipMemset(base + L.ctr, 0, L.ids - L.ctr);
     if (err == hipSuccess)
         err = hipDeviceSynchronize();
     if (err != hipSuccess)
@@ -312,30 +354,59 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     return MOE_OK;
 }
 
-extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits,
-                                     float *out, int32_t m, void *hip_stream)
+// Arguments of a run, checked before the handle is read. *skip is set for
+// m = 0 (nothing to enqueue).
+static moe_status check_run_args(moe_decode_t h, const void *x_bf16, const float *logits,
+                                 float *out, int32_t m, bool *skip)
 {
+    *skip = false;
     if (!h)
         return fail(MOE_E_INVALID, "handle is NULL");
-    if (m < 0 || m > h->max_tokens)
-        return fail(MOE_E_INVALID, "m = %d not in 0..max_tokens (%d)", m, h->max_tokens);
-    if (m == 0)
+    if (m < 0)
+        return fail(MOE_E_INVALID, "m = %d < 0", m);
+    if (m == 0) {
+        *skip = true;
         return MOE_OK;
+    }
     if (!x_bf16 || !logits || !out)
         return fail(MOE_E_INVALID, "NULL x, logits or out");
-    hipStream_t s = (hipStream_t)hip_stream;
+    // the kernels read x as bf16 pairs and logits as fp32, and write out in
+    // 16-byte pieces
+    if (!aligned(x_bf16, 4) || !aligned(logits, 4) || !aligned(out, 16))
+        return fail(MOE_E_INVALID, "misaligned x (needs 4 B), logits (4 B) or out (16 B)");
+    if (m > h->max_tokens)
+        return fail(MOE_E_INVALID, "m = %d not in 0..max_tokens (%d)", m, h->max_tokens);
+    return MOE_OK;
+}
+
+// Bind the handle to its stream on the first run; another stream later is
+// refused.
+static moe_status bind_stream(moe_decode_t h, hipStream_t s)
+{
     if (h->bound && s != h->stream)
         return fail(MOE_E_STREAM, "handle is bound to another stream");
     h->bound = true;
     h->stream = s;
-    Params p = h->p;
+    return MOE_OK;
+}
+
+// The per-run fields of the kernels' parameters for m tokens.
+static void run_params(const moe_decode_t h, Params &p, float *out, int m)
+{
     p.out = out;
     p.span1 = h->span1[m];
     p.gcap = h->gcap[m];
     p.lds_tab = h->lds_tab[m];
     p.egrid = h->grid[m];
+    p.group_rows = h->prefill[m] ? kPrefillRows : kGroupRows;
+}
+
+// Enqueue the kernels of one run (route, expert or the two prefill kernels,
+// combine) with the buffers p points at.
+static moe_status enqueue(moe_decode_t h, Params p, const void *x_bf16, const float *logits,
+                          int m, hipStream_t s)
+{
     const bool pf = h->prefill[m] != 0;
-    p.group_rows = pf ? kPrefillRows : kGroupRows;
     HIP_TRY(launch_route(p, (const uint16_t *)x_bf16, logits, m, s));
     if (h->ev_begin)
         HIP_TRY(hipEventRecord(h->ev_begin, s));
@@ -351,7 +422,23 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
     h->ran = true;
     h->last_m = m;
     h->last_prefill = pf;
+    h->last = p;
     return MOE_OK;
+}
+
+extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits,
+                                     float *out, int32_t m, void *hip_stream)
+{
+    bool skip;
+    moe_status st = check_run_args(h, x_bf16, logits, out, m, &skip);
+    if (st != MOE_OK || skip)
+        return st;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if ((st = bind_stream(h, s)) != MOE_OK)
+        return st;
+    Params p = h->p;
+    run_params(h, p, out, m);
+    return enqueue(h, p, x_bf16, logits, m, s);
 }
 
 extern "C" moe_status moe_decode_destroy(moe_decode_t h)
@@ -359,9 +446,13 @@ extern "C" moe_status moe_decode_destroy(moe_decode_t h)
     if (!h)
         return MOE_OK;
     hipError_t err = hipSuccess;
+    uint32_t error_word = 0;
     if (h->scratch) {
         if (h->bound)
             err = hipStreamSynchronize(h->stream);
+        if (err == hipSuccess && h->ran)
+            err = hipMemcpy(&error_word, &h->last.ctr->error_word, sizeof error_word,
+                            hipMemcpyDeviceToHost);
         hipError_t e2 = hipFree(h->scratch);
         if (err == hipSuccess)
             err = e2;
@@ -369,6 +460,8 @@ extern "C" moe_status moe_decode_destroy(moe_decode_t h)
     delete h;
     if (err != hipSuccess)
         return fail(MOE_E_HIP, "destroy: %s", hipGetErrorString(err));
+    if (error_word)
+        return fail(MOE_E_DEVICE, "destroy: the last run reported error word 0x%x", error_word);
     return MOE_OK;
 }
 
@@ -396,6 +489,7 @@ extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_
         return fail(MOE_E_INVALID, "unknown query item %d", what);
     if (!h->ran)
         return fail(MOE_E_INVALID, "no run yet");
+    const Params &r = h->last;  // the buffers of the last run
     const int m = h->last_m, np = m * p.k;
     size_t need = what == MOE_Q_ROUTING  ? (size_t)np * 8
                   : what == MOE_Q_BUCKETS ? (size_t)(2 * p.E + 1 + np) * 4
@@ -405,21 +499,21 @@ extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_
     HIP_TRY(hipStreamSynchronize(h->stream));
     char *dst = (char *)host_buf;
     if (what == MOE_Q_ROUTING) {
-        HIP_TRY(hipMemcpy(dst, p.ids, 4 * np, hipMemcpyDeviceToHost));
-        HIP_TRY(hipMemcpy(dst + 4 * np, p.wts, 4 * np, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst, r.ids, 4 * np, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst + 4 * np, r.wts, 4 * np, hipMemcpyDeviceToHost));
     } else if (what == MOE_Q_BUCKETS) {
-        HIP_TRY(hipMemcpy(dst, p.counts, 4 * p.E, hipMemcpyDeviceToHost));
-        HIP_TRY(hipMemcpy(dst + 4 * p.E, p.offsets, 4 * (p.E + 1), hipMemcpyDeviceToHost));
-        HIP_TRY(hipMemcpy(dst + 4 * (2 * p.E + 1), p.rows, 4 * np, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst, r.counts, 4 * p.E, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst + 4 * p.E, r.offsets, 4 * (p.E + 1), hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(dst + 4 * (2 * p.E + 1), r.rows, 4 * np, hipMemcpyDeviceToHost));
     } else {
         Plan plan;
         Counters c;
-        HIP_TRY(hipMemcpy(&plan, p.plan, sizeof plan, hipMemcpyDeviceToHost));
-        HIP_TRY(hipMemcpy(&c, p.ctr, sizeof c, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(&plan, r.plan, sizeof plan, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(&c, r.ctr, sizeof c, hipMemcpyDeviceToHost));
         moe_decode_stats st{};
         st.m = plan.m;
         std::vector<int32_t> counts(p.E);
-        HIP_TRY(hipMemcpy(counts.data(), p.counts, 4 * p.E, hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(counts.data(), r.counts, 4 * p.E, hipMemcpyDeviceToHost));
         st.hit_experts = 0;
         for (int32_t c : counts)
             st.hit_experts += c > 0;
@@ -431,6 +525,9 @@ extern "C" moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_
         st.items_done = (int32_t)done;
         st.error_word = (int32_t)c.error_word;
         memcpy(dst, &st, sizeof st);
+        if (c.error_word)
+            return fail(MOE_E_DEVICE, "the last run reported error word 0x%x (1: a dependency "
+                        "wait gave up; that run's output is NaN)", c.error_word);
     }
     return MOE_OK;
 }

@@ -20,13 +20,20 @@ def _align(n, a=256):
 
 
 def _blob(arrays, device):
-    """Concatenate byte views at 256-byte aligned offsets into one device tensor."""
-    offs, total = [], 0
+    """Concatenate byte views at 256-byte aligned offsets into one device tensor.
+    An array object passed more than once is stored once (its entries share
+    the offset)."""
+    offs, total, seen, first = [], 0, {}, []
     for a in arrays:
+        if id(a) in seen:
+            offs.append(seen[id(a)])
+            continue
+        seen[id(a)] = total
         offs.append(total)
+        first.append((a, total))
         total += _align(a.nbytes)
     host = np.zeros(max(total, 256), np.uint8)
-    for a, o in zip(arrays, offs):
+    for a, o in first:
         host[o:o + a.nbytes] = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
     dev = torch.from_numpy(host).to(device)
     return dev, offs
@@ -108,9 +115,31 @@ class DeviceLayer:
                     tot += N * Cc // 2 + N * Cc // 16
         return tot
 
+    def _check_args(self, x, logits, out, m):
+        """Shapes, dtypes, layout and device of run()'s tensors (the C ABI
+        takes raw pointers and cannot tell)."""
+        if m < 0:
+            raise ValueError(f"m = {m} < 0")
+        want = ((x, (torch.bfloat16, torch.int16), self.H, "x"),
+                (logits, (torch.float32,), self.E, "logits"),
+                (out, (torch.float32,), self.H, "out"))
+        for t, dtypes, cols, name in want:
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if t.dtype not in dtypes:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+            if t.dim() != 2 or t.shape[1] != cols or t.shape[0] < m:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [>= {m}, {cols}]")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous (row-major)")
+        for t, _, _, name in want:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} is on {t.device}, expected a GPU tensor")
+
     def run(self, x, logits, out, m=None, stream=None):
         """x: bf16 [m, H] (or int16 bit patterns), logits fp32 [m, E], out fp32 [m, H]."""
         m = x.shape[0] if m is None else m
+        self._check_args(x, logits, out, m)
         s = torch.cuda.current_stream() if stream is None else stream
         moe_decode_run(self.handle, x.data_ptr(), logits.data_ptr(), out.data_ptr(), m,
                        s.cuda_stream)
@@ -137,9 +166,11 @@ class DeviceLayer:
         return dict(counts=buf[:E], offsets=buf[E:2 * E + 1], rows=buf[2 * E + 1:])
 
     def close(self):
+        """Destroy the handle (raises MoeDecodeError if the last run reported a
+        device error; the handle is gone either way)."""
         if self.handle:
-            moe_decode_destroy(self.handle)
-            self.handle = None
+            h, self.handle = self.handle, None
+            moe_decode_destroy(h)
 
     def __del__(self):
         try:

@@ -63,6 +63,8 @@ typedef enum { MOE_FMT_CODEBOOK = 1, MOE_FMT_NVFP4 = 2 } moe_format;
  * MOE_FMT_CODEBOOK (bits = 2, 3 or 6): stand-in for the 2/3-bit codes of the
  * routed experts and the 6-bit codes of the dense linears that the pages
  * name but do not define (page "lna-lab/README.md", "What is in the pack").
+ * Routed experts take bits 2 or 3 (6 fails create with MOE_E_UNSUPPORTED);
+ * the shared expert takes 2, 3 or 6.
  * Weights live in the rotated basis (see signs_* below).
  *   codes  : uint32 words, bits words per slot (tile = 64*bits words),
  *            4-byte aligned. Column jj of a slot, code bits LSB first:
@@ -135,9 +137,28 @@ moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
  * Enqueue one decode step on `hip_stream` (a hipStream_t; NULL = default
  * stream). Asynchronous: no allocation, no host synchronisation, no tuning;
  * safe to capture into a HIP graph.
- *   x_bf16 : device bf16 [m][hidden], row-major.
- *   logits : device fp32 [m][num_experts], row-major; must be finite.
- *   out    : device fp32 [m][hidden], row-major; fully overwritten.
+ *   x_bf16 : device bf16 [m][hidden], row-major, 4-byte aligned.
+ *   logits : device fp32 [m][num_experts], row-major, 4-byte aligned; must be
+ *            finite.
+ *   out    : device fp32 [m][hidden], row-major, 16-byte aligned; fully
+ *            overwritten.
+ * Activation range: x~ (the rotated x) and h~ (the rotated h = SiLU(g)*u)
+ * are staged in fp16; products and sums are fp32. Results match the fp64
+ * definition within 2e-3 (per token, relative to the token's largest output)
+ * while every staged value stays below the fp16 maximum 65504. A rotated
+ * 128-block holds values of at most sqrt(128) times the block's largest
+ * input, so it suffices that |x| < 5790 and |SiLU(g)*u| < 5790 (codebook
+ * format; NVFP4 rotates nothing: |x|, |SiLU(g)*u| < 65504). g and u scale
+ * with x, so h grows with the square of the activations' scale. Staged
+ * values beyond the range become inf.
+ * The expert kernel is persistent: its grid is the number of its blocks
+ * that fit on the device at once, and its down work waits (bounded) for
+ * gate/up work of other blocks. It therefore assumes every block of its grid
+ * becomes resident; work of other streams or processes that holds compute
+ * units for the whole run can keep some blocks from starting. If a wait
+ * gives up (about 2 s), the run writes NaN to `out` and the next
+ * moe_decode_query(MOE_Q_STATS) or moe_decode_destroy() returns
+ * MOE_E_DEVICE.
  *   m      : 0..max_tokens. m = 0 returns MOE_OK and enqueues nothing.
  * The handle binds to the first stream it runs on; a different stream later
  * returns MOE_E_STREAM (page "LNA-CANON.md", "lna2 とは": concurrent streams
@@ -153,8 +174,10 @@ moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
 moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits, float *out,
                           int32_t m, void *hip_stream);
 
-/* Free the handle's scratch and the handle. NULL is accepted. Graphs that
- * captured runs of the handle must not be replayed afterwards. */
+/* Free the handle's scratch and the handle (after synchronising its stream).
+ * NULL is accepted. Graphs that captured runs of the handle must not be
+ * replayed afterwards. Returns MOE_E_DEVICE (after freeing) if the last run
+ * reported a kernel error. */
 moe_status moe_decode_destroy(moe_decode_t h);
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
@@ -189,7 +212,8 @@ typedef struct {
 
 /* Copy the requested item into host_buf (host, `bytes` long). Errors:
  * MOE_E_INVALID (unknown item, NULL buffer, buffer too small, no run yet for
- * ROUTING/BUCKETS/STATS), MOE_E_HIP. */
+ * ROUTING/BUCKETS/STATS), MOE_E_HIP, MOE_E_DEVICE (MOE_Q_STATS only: the
+ * stats are copied, and error_word of the last run is nonzero). */
 moe_status moe_decode_query(moe_decode_t h, int32_t what, void *host_buf, size_t bytes);
 
 /*

@@ -27,6 +27,8 @@ class Workload:
     layers: int = 1
     zipf_s: float = 1.1
     shared_bits: int = 0    # > 0: an always-on shared expert with these codebook bits
+    nv_scales: str = "exp6to8"  # NVFP4 block scales: "exp6to8" (0.5..3.75) or "all_finite"
+    ts_scale: float = 0.004     # NVFP4 tensor scale = ts_scale * U(0.8, 1.2)
 
     @property
     def max_tokens(self) -> int:
@@ -74,7 +76,9 @@ WORKLOADS = {
 
 
 def small_workload(name, num_experts, top_k, hidden, inter, fmt="codebook",
-                   bits_mix="alternate", router="normal", config_id=100, shared_bits=0):
+                   bits_mix="alternate", router="normal", config_id=100, shared_bits=0,
+                   nv_scales="exp6to8", ts_scale=0.004):
     """A reduced shape for fast tests (same recipe, smaller sizes)."""
     return Workload(name, config_id, num_experts, top_k, hidden, inter, fmt, bits_mix,
-                    router, (1,), shared_bits=shared_bits)
+                    router, (1,), shared_bits=shared_bits, nv_scales=nv_scales,
+                    ts_scale=ts_scale)

@@ -10,8 +10,10 @@ stored weight is drawn directly in its stored form:
 * group scales: fp16 of U(0.01, 0.05).
 * NVFP4 codes: uniform random bytes (two e2m1 nibbles each).
 * NVFP4 block scales: e4m3fn bytes with exponent field 6..8 and any mantissa,
-  i.e. values in [0.5, 3.75].
-* NVFP4 tensor scale: fp32 of 0.004 * U(0.8, 1.2).
+  i.e. values in [0.5, 3.75]; or (workload option "all_finite") uniform over
+  all 254 finite e4m3fn codes of either sign, subnormals and 448 included.
+* NVFP4 tensor scale: fp32 of ts_scale * U(0.8, 1.2), ts_scale 0.004 unless
+  the workload says otherwise.
 * activations: N(0,1) rounded to bfloat16 (round to nearest even), given as the
   raw 16-bit patterns.
 * router logits: fp32 N(0,1), plus a per-expert Zipf bias -s*ln(rank) for the
@@ -129,10 +131,15 @@ def make_tensor(w: Workload, layer: int, e: int, proj: int, bits: int) -> dict:
     nbytes = N * C // 2
     codes = _raw_words(cid, nbytes // 4, layer, TAG_CODES, e, proj).view(np.uint8)
     g = _rng(cid, layer, TAG_SCALES, e, proj)
-    ex = g.integers(6, 9, N * C // 16)
-    mant = g.integers(0, 8, N * C // 16)
-    scales = ((ex << 3) | mant).astype(np.uint8)
-    ts = np.float32(0.004 * _rng(cid, layer, TAG_TSCALE, e, proj).uniform(0.8, 1.2))
+    if w.nv_scales == "all_finite":
+        # every e4m3fn byte except the two NaN codes 0x7F and 0xFF
+        finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+        scales = finite[g.integers(0, len(finite), N * C // 16)]
+    else:
+        ex = g.integers(6, 9, N * C // 16)
+        mant = g.integers(0, 8, N * C // 16)
+        scales = ((ex << 3) | mant).astype(np.uint8)
+    ts = np.float32(w.ts_scale * _rng(cid, layer, TAG_TSCALE, e, proj).uniform(0.8, 1.2))
     return dict(bits=4, codes=codes, scales=scales, lut=None, tensor_scale=ts)
 
 

@@ -24,6 +24,8 @@ def to_dev(case, m=None):
     x = torch.from_numpy(case["x"].view(np.int16)).cuda()
     lg = torch.from_numpy(case["logits"]).cuda()
     out = torch.full((x.shape[0], case["workload"].hidden), float("nan"), device="cuda")
+    # the copies and the fill ran on the current stream; runs may use another
+    torch.cuda.synchronize()
     return x, lg, out
 
 
@@ -49,3 +51,36 @@ def check_routing(layer, case, m):
     assert np.array_equal(b["offsets"], rb["offsets"])
     k = case["workload"].top_k
     assert np.array_equal(b["rows"], rb["rows_t"] * k + rb["rows_j"])
+
+
+def routed_case(w, m, layer=0, x=None, logits=None):
+    """A case whose stored tensors cover only the experts its tokens route to
+    (the oracle never reads the others; large layers generate quickly)."""
+    from moe_synth import gen
+    lg = gen.make_logits(w, layer, m) if logits is None else logits
+    ids, _ = oracle.route(lg, w.top_k)
+    d = gen.make_layer(w, layer, experts=np.unique(ids))
+    d.update(workload=w, layer=layer, m=m, x=gen.make_x(w, layer, m) if x is None else x,
+             logits=lg)
+    return d
+
+
+def device_layer(case, max_tokens=None):
+    """DeviceLayer for a case that may lack unrouted experts: those point at
+    one routed expert's tensors (uploaded once; the kernels never read them)."""
+    w = case["workload"]
+    tensors = dict(case["tensors"])
+    have = sorted({e for e, _ in tensors})
+    for e in range(w.num_experts):
+        if e not in have:
+            for p in range(3):
+                tensors[(e, p)] = case["tensors"][(have[0], p)]
+    c = dict(case, tensors=tensors)
+    return DeviceLayer.from_case(c, max_tokens=max_tokens or case["x"].shape[0])
+
+
+def check_stats(layer):
+    st = layer.stats()   # raises MoeDecodeError(MOE_E_DEVICE) on a kernel error
+    assert st.error_word == 0 and st.items_done == st.items, (st.error_word, st.items_done,
+                                                               st.items)
+    return st

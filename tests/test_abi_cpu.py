@@ -154,3 +154,55 @@ def test_binding_is_marshalling_only():
             src = open(os.path.join(pkg, f)).read()
             assert "oracle" not in src.replace("oracle/", ""), f
             assert "import oracle" not in src
+
+
+def test_create_rejects_routed_six_bit_codes():
+    # 6-bit codes are the shared expert's stored form only; a routed expert
+    # with them is refused before any HIP call
+    st, err = create_status(make_cfg(bits=6))
+    assert st == B.MOE_E_UNSUPPORTED and "shared expert only" in err
+
+
+def test_run_checks_pointer_arguments_before_the_handle():
+    # The pointer checks come before the handle is read, so a handle value
+    # that is never dereferenced is enough to reach them without a GPU.
+    L = B.lib()
+    fake_handle = C.c_void_p(FAKE)
+    cases = [
+        ((FAKE, FAKE, FAKE, -1), "m = -1"),
+        ((None, FAKE, FAKE, 1), "NULL"),
+        ((FAKE, None, FAKE, 1), "NULL"),
+        ((FAKE, FAKE, None, 1), "NULL"),
+        ((FAKE + 2, FAKE, FAKE, 1), "misaligned"),
+        ((FAKE, FAKE + 2, FAKE, 1), "misaligned"),
+        ((FAKE, FAKE, FAKE + 4, 1), "misaligned"),     # out needs 16-byte alignment
+    ]
+    for (x, lg, out, m), msg in cases:
+        assert L.moe_decode_run(fake_handle, x, lg, out, m, None) == B.MOE_E_INVALID
+        assert msg in B.moe_decode_last_error(), (x, lg, out, m)
+    # m = 0 enqueues nothing and succeeds whatever the pointers
+    assert L.moe_decode_run(fake_handle, None, None, None, 0, None) == B.MOE_OK
+
+
+def test_device_layer_checks_run_arguments():
+    import torch
+    from bit_quantized_moe_block_amd import DeviceLayer
+    layer = DeviceLayer.__new__(DeviceLayer)   # argument checks only: no handle, no device
+    layer.H, layer.E, layer.handle = 256, 8, None
+    x = torch.zeros(2, 256, dtype=torch.bfloat16)
+    lg = torch.zeros(2, 8, dtype=torch.float32)
+    out = torch.zeros(2, 256, dtype=torch.float32)
+    with pytest.raises(TypeError, match="dtype"):
+        layer._check_args(x.float(), lg, out, 2)
+    with pytest.raises(TypeError, match="dtype"):
+        layer._check_args(x, lg.double(), out, 2)
+    with pytest.raises(ValueError, match="shape"):
+        layer._check_args(x[:, :128], lg, out, 2)
+    with pytest.raises(ValueError, match="shape"):
+        layer._check_args(x, lg, out, 3)
+    with pytest.raises(ValueError, match="contiguous"):
+        layer._check_args(x, lg, torch.zeros(256, 2).t(), 2)
+    with pytest.raises(ValueError, match="GPU"):
+        layer._check_args(x, lg, out, 2)
+    with pytest.raises(ValueError, match="< 0"):
+        layer._check_args(x, lg, out, -1)

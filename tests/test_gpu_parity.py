@@ -4,6 +4,7 @@ Sizes the oracle finishes in seconds cover several tiles and ragged tails;
 the full-size workloads are checked on sampled tokens (every expert FFN of
 those tokens, every output element) plus exact routing for all tokens.
 """
+import ctypes as C
 import dataclasses
 
 import numpy as np
@@ -13,7 +14,8 @@ import torch
 import oracle
 from bit_quantized_moe_block_amd import DeviceLayer
 from moe_synth import WORKLOADS, gen, small_workload
-from tests.gpu_common import REL_TOL, check_routing, rel_err, run_gpu, say, to_dev
+from tests.gpu_common import (REL_TOL, check_routing, check_stats, rel_err, run_gpu, say,
+                              to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +35,7 @@ def parity(case, tokens=None, max_tokens=None):
     try:
         out = run_gpu(layer, case)
         check_routing(layer, case, m)
-        st = layer.stats()
-        assert st.error_word == 0 and st.items_done == st.items
+        check_stats(layer)
         ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
         err = rel_err(out, ref["out"], tokens)
         say(f"    rel={err:.3e}")
@@ -78,24 +79,6 @@ def full_layer():
     layer = DeviceLayer.from_case(d, max_tokens=w.max_tokens)
     yield d, layer
     layer.close()
-
-
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 24])
-def test_full_layer_sampled(full_layer, m):
-    d, layer = full_layer
-    w = d["workload"]
-    case = dict(d, m=m, x=gen.make_x(w, 0, m), logits=gen.make_logits(w, 0, m))
-    say(f"[parity] full_layer m={m}")
-    out = run_gpu(layer, case)
-    check_routing(layer, case, m)
-    st = layer.stats()
-    assert st.error_word == 0 and st.items_done == st.items
-    tokens = sorted(set([0, m - 1, m // 2]))
-    ref = oracle.Layer.from_case(case).run(case["x"], case["logits"], tokens=tokens)
-    err = rel_err(out, ref["out"], tokens)
-    say(f"    rel={err:.3e} hit={st.hit_experts} items={st.items}")
-    assert err <= REL_TOL
-    assert np.all(np.isfinite(out))
 
 
 @pytest.mark.parametrize("m", [16, 24])
@@ -224,15 +207,24 @@ def test_bitwise_repeatable_and_graph_replay():
     layer = DeviceLayer.from_case(case, max_tokens=24)
     try:
         x, lg, out = to_dev(case)
+        # a second input between the repeats: stale partial sums of another
+        # run would show
+        cb = gen.make_case(w, 24, layer=1)
+        xb, lgb, outb = to_dev(dict(case, x=cb["x"], logits=cb["logits"]))
         outs = []
         with torch.cuda.stream(s):
             for _ in range(10):
                 out.fill_(float("nan"))
                 layer.run(x, lg, out, stream=s)
                 s.synchronize()
+                check_stats(layer)
                 outs.append(out.clone())
+                layer.run(xb, lgb, outb, stream=s)
+                s.synchronize()
+                check_stats(layer)
         for o in outs[1:]:
             assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+        assert not torch.equal(outb, outs[0])
         g = torch.cuda.CUDAGraph()
         out_g = torch.full_like(out, float("nan"))
         with torch.cuda.graph(g, stream=s):
@@ -305,9 +297,14 @@ def test_m_zero_and_range_errors():
         layer.run(x, lg, out, m=0)
         torch.cuda.synchronize()
         assert torch.all(out == 7.0)
+        # m beyond max_tokens: refused by the library (through the raw call)
+        # and by the binding's shape check before it
         with pytest.raises(B.MoeDecodeError) as ei:
+            B.moe_decode_run(layer.handle, x.data_ptr(), lg.data_ptr(), out.data_ptr(), 3,
+                             torch.cuda.current_stream().cuda_stream)
+        assert ei.value.status == B.MOE_E_INVALID and "max_tokens" in str(ei.value)
+        with pytest.raises(ValueError):
             layer.run(x, lg, out, m=3)
-        assert ei.value.status == B.MOE_E_INVALID
         layer.run(x, lg, out)                # first real run binds the current stream
         torch.cuda.synchronize()
         other = torch.cuda.Stream()
@@ -485,3 +482,75 @@ def test_nvfp4_prefill_layer_sampled():
         assert err <= REL_TOL
     finally:
         dl.close()
+
+
+# Activations well away from N(0,1): x * 8 plus a few outliers of +-500 in
+# every token. The staged x~ and h~ stay inside the fp16 range that the
+# header states (|x| < 5790, |SiLU(g) u| < 5790); both expert paths.
+RANGE = [
+    (small_workload("rng1", 32, 4, 1024, 256, bits_mix="alternate", config_id=501), 16),
+    (small_workload("rng2", 32, 4, 1024, 256, bits_mix="all3", router="zipf", config_id=502), 64),
+    (small_workload("rng3", 16, 2, 512, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=503), 12),
+    (small_workload("rng4", 16, 2, 512, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=504), 80),
+]
+
+
+@pytest.mark.parametrize("w,m", RANGE, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_large_magnitude_activations(w, m):
+    case = gen.make_case(w, m)
+    rng = np.random.default_rng(w.config_id)
+    x = rng.standard_normal((m, w.hidden)).astype(np.float32) * 8.0
+    for t in range(m):
+        cols = rng.choice(w.hidden, 3, replace=False)
+        x[t, cols] = rng.choice([-500.0, 500.0], 3)
+    case["x"] = gen.bf16_bits_from_f32(x)
+    layer, out = parity(case)
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out)) > 10.0   # the scale did reach the output
+
+
+# NVFP4 block scales drawn over every finite e4m3 code (either sign,
+# subnormals, 448), on both expert paths.
+NV_ALL = [
+    (small_workload("nva1", 16, 4, 1024, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=511,
+                    nv_scales="all_finite", ts_scale=0.0002), 9),
+    (small_workload("nva2", 32, 8, 512, 384, fmt="nvfp4", bits_mix="nvfp4", router="zipf",
+                    config_id=512, nv_scales="all_finite", ts_scale=0.0002), 24),
+    (small_workload("nva3", 16, 4, 512, 256, fmt="nvfp4", bits_mix="nvfp4", config_id=513,
+                    nv_scales="all_finite", ts_scale=0.0002), 100),
+]
+
+
+@pytest.mark.parametrize("w,m", NV_ALL, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_nvfp4_every_finite_scale_code(w, m):
+    case = gen.make_case(w, m)
+    codes = np.unique(np.concatenate([t["scales"] for t in case["tensors"].values()]))
+    assert len(codes) == 254   # every finite code occurs
+    parity(case)
+
+
+def test_gave_up_wait_surfaces_as_device_error(monkeypatch):
+    # A bound of zero polls makes the down items' wait for h give up at
+    # once (every kernel still ends normally): the run's output must be NaN,
+    # the stats query and destroy must return MOE_E_DEVICE, and a handle
+    # with the normal bound must run the same inputs correctly afterwards.
+    import bit_quantized_moe_block_amd as B
+    w = small_workload("spin", 64, 8, 1024, 512, bits_mix="alternate", config_id=520)
+    case = gen.make_case(w, 8)
+    monkeypatch.setenv("MOE_DECODE_SPIN_LIMIT", "0")
+    layer = DeviceLayer.from_case(case, max_tokens=8)
+    monkeypatch.delenv("MOE_DECODE_SPIN_LIMIT")
+    try:
+        out = run_gpu(layer, case)
+        with pytest.raises(B.MoeDecodeError) as ei:
+            layer.stats()
+        assert ei.value.status == B.MOE_E_DEVICE
+        st = B.moe_decode_stats()
+        B.lib().moe_decode_query(layer.handle, B.MOE_Q_STATS, C.byref(st), C.sizeof(st))
+        assert st.error_word == 1
+        assert np.all(np.isnan(out))
+    finally:
+        with pytest.raises(B.MoeDecodeError) as ei:
+            layer.close()
+        assert ei.value.status == B.MOE_E_DEVICE
+    parity(case)
