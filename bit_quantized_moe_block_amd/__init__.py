@@ -17,8 +17,9 @@ MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_HIP, MOE_E_NOMEM, MOE_E_STREAM, 
 MOE_FMT_CODEBOOK, MOE_FMT_NVFP4 = 1, 2
 MOE_Q_INFO, MOE_Q_ROUTING, MOE_Q_BUCKETS, MOE_Q_STATS = 1, 2, 3, 4
 
-EXPORTED = ("moe_decode_create", "moe_decode_run", "moe_decode_destroy",
-            "moe_decode_last_error", "moe_decode_query", "moe_decode_profile_events")
+EXPORTED = ("moe_decode_create", "moe_decode_run", "moe_decode_run_static",
+            "moe_decode_destroy", "moe_decode_last_error", "moe_decode_query",
+            "moe_decode_profile_events")
 
 
 class moe_tensor_desc(C.Structure):
@@ -68,6 +69,9 @@ def lib():
         L.moe_decode_run.restype = C.c_int
         L.moe_decode_run.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                      C.c_void_p]
+        L.moe_decode_run_static.restype = C.c_int
+        L.moe_decode_run_static.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_int32, C.c_void_p]
         L.moe_decode_destroy.restype = C.c_int
         L.moe_decode_destroy.argtypes = [C.c_void_p]
         L.moe_decode_last_error.restype = C.c_char_p
@@ -100,6 +104,11 @@ def moe_decode_create(cfg):
 def moe_decode_run(h, x_ptr, logits_ptr, out_ptr, m, stream_ptr):
     """All pointers are device addresses (ints); stream_ptr a hipStream_t (int)."""
     return _check(lib().moe_decode_run(h, x_ptr, logits_ptr, out_ptr, m, stream_ptr))
+
+
+def moe_decode_run_static(h, x_ptr, logits_ptr, out_ptr, m, stream_ptr):
+    """moe_decode_run with the per-run buffers in the library's static scratch."""
+    return _check(lib().moe_decode_run_static(h, x_ptr, logits_ptr, out_ptr, m, stream_ptr))
 
 
 def moe_decode_destroy(h):

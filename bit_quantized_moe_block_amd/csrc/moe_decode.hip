@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -153,6 +154,41 @@ static void bind_scratch(Params &p, char *base, const Layout &L)
     p.y_part = (float *)(base + L.y);
 }
 
+// Static scratch of moe_decode_run_static(): one block per device (each GPU
+// holds its own copy of this array from the library's load until the process
+// ends). Every static run on a device uses it, so runs that overlap on one
+// device race. Host code uses the address that hipGetSymbolAddress gives for
+// the current device, never the array's name (a host-side stand-in).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_static_mu;
+static void *g_static_ptr[kMaxDevices] = {};
+
+// Once per device, with that device current (called by create): the device
+// address of its static scratch, and its counters cleared (the route kernel's
+// top-k hand-off counter must start at zero; every run leaves it at zero, and
+// each run writes every other buffer before reading it).
+static moe_status static_scratch_init(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return fail(MOE_E_UNSUPPORTED, "device %d beyond the %d supported", device, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (g_static_ptr[device])
+        return MOE_OK;
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return fail(MOE_E_HIP, "hipGetSymbolAddress(static scratch) failed: %s", hipGetErrorString(e));
+    e = hipMemset(ptr, 0, sizeof(Counters));
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+        return fail(MOE_E_HIP, "clearing the static scratch failed: %s", hipGetErrorString(e));
+    g_static_ptr[device] = ptr;
+    return MOE_OK;
+}
+
 static moe_status validate(const moe_decode_config *c)
 {
     if (!c)
@@ -282,6 +318,11 @@ extern "C" moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode
     if (err != hipSuccess)
         return cleanup(fail(MOE_E_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(err)));
     h->cu_count = prop.multiProcessorCount;
+    {
+        const moe_status ss = static_scratch_init(h->device);
+        if (ss != MOE_OK)
+            return cleanup(ss);
+    }
 
     // The handle's scratch: the per-run buffers for max_tokens, then the
     // device copy of the descriptor table.
@@ -438,6 +479,33 @@ extern "C" moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const f
         return st;
     Params p = h->p;
     run_params(h, p, out, m);
+    return enqueue(h, p, x_bf16, logits, m, s);
+}
+
+extern "C" moe_status moe_decode_run_static(moe_decode_t h, const void *x_bf16,
+                                            const float *logits, float *out, int32_t m,
+                                            void *hip_stream)
+{
+    bool skip;
+    moe_status st = check_run_args(h, x_bf16, logits, out, m, &skip);
+    if (st != MOE_OK || skip)
+        return st;
+    void *base = g_static_ptr[h->device];  // set by create for this device
+    if (!base)
+        return fail(MOE_E_INVALID, "no static scratch on device %d", h->device);
+    Params p = h->p;
+    run_params(h, p, out, m);
+    // the buffers sized for this run: m tokens, m (k + shared) bucket rows
+    p.pair_cap = m * (p.k + p.has_shared);
+    const Layout L = scratch_layout(p, m, p.pair_cap, group_cap(p, m));
+    if (L.end > kStaticScratchBytes)
+        return fail(MOE_E_UNSUPPORTED,
+                    "a run of %d tokens needs %zu bytes of static scratch, more than its %zu", m,
+                    L.end, kStaticScratchBytes);
+    hipStream_t s = (hipStream_t)hip_stream;
+    if ((st = bind_stream(h, s)) != MOE_OK)
+        return st;
+    bind_scratch(p, (char *)base, L);
     return enqueue(h, p, x_bf16, logits, m, s);
 }
 

@@ -12,7 +12,7 @@ import torch
 from . import (MOE_DECODE_ABI_VERSION, MOE_FMT_CODEBOOK, MOE_FMT_NVFP4, MOE_Q_BUCKETS,
                MOE_Q_INFO, MOE_Q_ROUTING, MOE_Q_STATS, moe_decode_config, moe_decode_create,
                moe_decode_destroy, moe_decode_info, moe_decode_query, moe_decode_run,
-               moe_decode_stats, moe_tensor_desc)
+               moe_decode_run_static, moe_decode_stats, moe_tensor_desc)
 
 
 def _align(n, a=256):
@@ -143,6 +143,15 @@ class DeviceLayer:
         s = torch.cuda.current_stream() if stream is None else stream
         moe_decode_run(self.handle, x.data_ptr(), logits.data_ptr(), out.data_ptr(), m,
                        s.cuda_stream)
+
+    def run_static(self, x, logits, out, m=None, stream=None):
+        """run() with the per-run buffers in the library's static scratch (no
+        allocation; static runs on one device must not overlap)."""
+        m = x.shape[0] if m is None else m
+        self._check_args(x, logits, out, m)
+        s = torch.cuda.current_stream() if stream is None else stream
+        moe_decode_run_static(self.handle, x.data_ptr(), logits.data_ptr(), out.data_ptr(), m,
+                              s.cuda_stream)
 
     def info(self):
         i = moe_decode_info()

@@ -174,6 +174,27 @@ moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
 moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits, float *out,
                           int32_t m, void *hip_stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as moe_decode_run(), same arguments, same kernels and bitwise the
+ * same results, with every per-run buffer (routing, buckets, work plan,
+ * counters, rotated activations, partial sums) in the library's static
+ * scratch instead of the handle's: one 32 MiB block per device, held from
+ * the library's load until the process ends, whose address create() looks
+ * up once per device. It allocates nothing and calls no allocating routine.
+ * Every static run on a device uses that one block (page "LNA-CANON.md",
+ * section "lna2 とは": one scratch per device), so static runs that overlap
+ * on one device race: runs of any handles must be ordered (one stream).
+ * A run whose buffers exceed the block (at 256 experts, top-8, hidden 4096,
+ * inter 2048: more than 39 tokens, or 35 with a shared expert) fails with
+ * MOE_E_UNSUPPORTED before anything is enqueued. Queries
+ * after a static run read the block, so they see that run only until the
+ * next static run on the device. Errors: as moe_decode_run().
+ */
+moe_status moe_decode_run_static(moe_decode_t h, const void *x_bf16, const float *logits,
+                                 float *out, int32_t m, void *hip_stream);
+
 /* Free the handle's scratch and the handle (after synchronising its stream).
  * NULL is accepted. Graphs that captured runs of the handle must not be
  * replayed afterwards. Returns MOE_E_DEVICE (after freeing) if the last run
