@@ -1364,16 +1364,17 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p)
 // cut into row groups of up to 64 rows, and each decoded weight step feeds
 // one MFMA per 16-row subtile of the group (up to four): the decode, the VALU
 // cost of these formats, is paid once per 64 rows instead of once per 16. A block
-// covers one row group and 128 output rows (of gate and of up: four waves
-// each) or 256 (down), over all input columns, so there are no column splits
+// covers one row group and 128 output rows (of gate and of up: eight waves
+// of one 16-row tile each) or 256 (down: sixteen waves), over all input
+// columns, so there are no column splits
 // and no partial sums. The gate/up block finishes SiLU(g) u and the h
 // rotation of its 128 rows itself (exactly one rotation block); the down
 // block writes y; the combine kernel sums the slots. The down kernel runs
 // after the gate/up kernel in stream order.
 
-constexpr int kPfThreads = 512;                   // 8 waves: 4 per projection (gate/up)
+constexpr int kPfThreads = 1024;                  // 16 waves: 8 per projection (gate/up)
 constexpr int kPfWaves = kPfThreads / 64;
-constexpr int kPfNT = 2;                          // 16-row tiles per wave
+constexpr int kPfNT = 1;                          // 16-row tiles per wave
 constexpr int kPfRows = 64;                       // rows of a prefill row group
 constexpr int kPfSub = kPfRows / 16;              // MFMA subtiles per row group
 constexpr int kPfAStride = 128 + kLdsPadHalves;   // staged chunk row stride (halves)
@@ -1382,7 +1383,7 @@ constexpr size_t kPfLds = 2 * kPfRows * kPfAStride * sizeof(_Float16);
 
 // One 128-column chunk of the first ROWS activation rows of the group (the
 // rows of its NSUB subtiles, ROWS = 16 NSUB): ROWS x 128 fp16 = 16 ROWS
-// 16-byte pieces, piece i by thread i mod 512; rows past R repeat row R-1
+// 16-byte pieces, piece i by thread i mod 1024; rows past R repeat row R-1
 // (their results are never stored). A piece index past the end skips whole
 // waves (256 pieces = 4 waves). Gate/up rows are tokens: lane r of every
 // wave holds the token of row r. Down rows off .. off+R-1 of h~ are
@@ -1443,31 +1444,22 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t w, _Float16 f)
 // instance: per-subtile branches inside the loop cost more issue slots than
 // the MFMAs they skip). Per step: the subtiles' A operands, then per tile one
 // decode and NSUB MFMAs; staged rows past R repeat row R-1 and their results
-// are never stored. The
-// decoded weights carry the group scale already (fp16 entry x scale, one more
-// fp16 rounding, as the NVFP4 block scale), so the accumulators take the
-// products directly: per-group partial results for every (tile, subtile)
-// would not fit in the registers.
+// are never stored. Codebook: the group's MFMA sums are scaled by the fp16
+// group scale in fp32 and added to the accumulators, as in the decode kernel
+// (the scaled weight is never rounded). NVFP4: the e4m3 block scale is exact
+// in the fp16 operand, so the MFMAs accumulate directly.
 template <int CLASS, int FMT, int NSUB>
 __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const _Float16 *A,
-                                         const u32x4 lut, floatx4 (&acc)[kPfNT][NSUB])
+                                         const uint32_t (&tab)[4], floatx4 (&acc)[kPfNT][NSUB])
 {
     const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
-    // codebook: the lane's tile tables hold codebook entry x group scale
-    // (fp16), so a lookup yields the scaled weight: the same fp16 value as
-    // scaling each decoded weight, for 2 (K = 2) or 4 (K = 3) multiplies and
-    // the byte split per tile and group instead of four per decoded step
-    uint32_t tab[kPfNT][4] = {};
+    floatx4 cc[kPfNT][NSUB];
     if constexpr (FMT != 4)
 #pragma unroll
-        for (int i = 0; i < kPfNT; ++i) {
-            const _Float16 f = __builtin_bit_cast(_Float16, (uint16_t)b.sc[i]);
-            u32x4 sl = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
-            for (int k = 0; k < (FMT == 3 ? 4 : 2); ++k)
-                sl[k] = scale_pair(lut[k], f);
-            lut_tables(sl, tab[i]);
-        }
+            for (int t = 0; t < NSUB; ++t)
+                cc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         half8 a[NSUB];
@@ -1482,12 +1474,26 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
                                                     : __builtin_amdgcn_cvt_f32_fp8(b.sc[i], 1));
                 bs = half2v{v, v};
             }
-            const half8 bv = decode_step<FMT>(b.w[i], s, tab[i], bs);
+            const half8 bv = decode_step<FMT>(b.w[i], s, tab, bs);
 #pragma unroll
-            for (int t = 0; t < NSUB; ++t)
-                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
+            for (int t = 0; t < NSUB; ++t) {
+                if constexpr (FMT == 4)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
+                else
+                    cc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, cc[i][t], 0, 0, 0);
+            }
         }
     }
+    if constexpr (FMT != 4)
+#pragma unroll
+        for (int i = 0; i < kPfNT; ++i) {
+            const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[i]);
+#pragma unroll
+            for (int t = 0; t < NSUB; ++t) {
+                acc[i][t] += f * cc[i][t];
+                asm volatile("" : "+v"(acc[i][t]));
+            }
+        }
 }
 
 // The main loop and epilogue of a prefill block, for one code format: FMT =
@@ -1515,6 +1521,10 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
     load_group<CLASS, KB, kPfNT>(bA, J, 0, lane, sc_lane);
     st.commit(pf_lds);
     load_group<CLASS, KB, kPfNT>(bB, J, min(1, G1), lane, sc_lane);
+    // the codebook's byte tables for the v_perm lookups (unscaled entries)
+    uint32_t tab[4] = {0, 0, 0, 0};
+    if constexpr (is_cb<CLASS>)
+        lut_tables(lut, tab);
     __syncthreads();
 
     floatx4 acc[kPfNT][NSUB];
@@ -1531,7 +1541,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
         _Float16 *Anext = (c & 1) ? half0 : half1;
         st.issue(p, DOWN, min(c + 1, G1));
         if (c < J.G)
-            pf_group<CLASS, FMT, NSUB>(b, A, lut, acc);
+            pf_group<CLASS, FMT, NSUB>(b, A, tab, acc);
         load_group<CLASS, KB, kPfNT>(b, J, min(c + 2, G1), lane, sc_lane);
         st.commit(Anext);
         __syncthreads();
@@ -1574,10 +1584,10 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
                 }
     } else {
         // h = silu(g) u through LDS (the up waves' u, then the gate waves'
-        // h in place), then each wave rotates the h of tokens wave, wave+4, ...
+        // h in place), then each wave rotates the h of rows wave, wave + 16, ...
         float *hb = (float *)pf_lds;  // [64 rows][kPfHStride]
-        const int lr0 = (wave & 3) * (kPfNT * 16);
-        if (wave >= 4)
+        const int lr0 = (wave & 7) * (kPfNT * 16);
+        if (wave >= 8)
 #pragma unroll
             for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
@@ -1589,7 +1599,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
                             hb[row * kPfHStride + lr0 + 16 * i + r16] = acc[i][t][j];
                     }
         __syncthreads();
-        if (wave < 4)
+        if (wave < 8)
 #pragma unroll
             for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
@@ -1657,7 +1667,7 @@ void prefill_kernel(Params p)
         const int qrow = off + min(lane, R - 1);
         tok = qrow < m * p.k ? p.rows[qrow] / p.k : qrow - m * p.k;
     }
-    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave >> 2)];
+    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave >> 3)];
     WaveJob J;
     J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
     J.scales = (gu8p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.scales);
@@ -1665,7 +1675,7 @@ void prefill_kernel(Params p)
     J.ts = __uint_as_float((uint32_t)uniform((int)__float_as_uint(d.tensor_scale)));
     J.bits = uniform(d.bits);
     J.G = DOWN ? p.I / 128 : p.H / 128;
-    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 3) * kPfNT;
+    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 7) * kPfNT;
     J.g0 = 0;
     const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
 
