@@ -7,6 +7,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoedecode.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("moe_decode.hip", "kernels.hip")]
+# measurement probes (plain streaming read, empty kernels), a library of their own
+PROBE_LIB = os.path.join(HERE, "libmoeprobe.so")
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "probes.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,8 +22,14 @@ FLAGS = [
 
 
 def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    _build_one(LIB, SOURCES, verbose)
+    _build_one(PROBE_LIB, PROBE_SOURCES, verbose)
+    return LIB
+
+
+def _build_one(lib, sources, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -28,11 +37,10 @@ def build(verbose=False):
                     if "packed-fp32-ops' is not a recognized feature" not in l)
     if r.returncode != 0:
         sys.stderr.write(out + "\n")
-        raise RuntimeError("hipcc failed building libmoedecode.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

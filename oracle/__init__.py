@@ -70,6 +70,7 @@ def lib():
         L.orc_moe_layer.argtypes = [P, C.c_int, P, P, P, P, P, P, P]
         L.orc_dequant.argtypes = [P, C.c_int, C.c_int, C.c_int, C.c_int, P]
         L.orc_expert.argtypes = [P, C.c_int, P, P]
+        L.orc_set_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
 
@@ -174,6 +175,11 @@ class Layer:
         if want_pairs:
             r["y_pairs"] = yp
         return r
+
+
+def set_threads(n):
+    """OpenMP threads of later oracle calls on this thread (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- scalars

@@ -471,6 +471,18 @@ int orc_moe_layer(const orc_layer *L, int m, const uint16_t *x_bf16, const float
     return used;
 }
 
+/* Threads of the OpenMP regions that follow on the calling thread (timing
+ * the baseline on one core); n < 1 leaves the setting alone. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Dense dequantisation of one stored matrix (for small checks). */
 void orc_dequant(const orc_layer *L, int e, int p, int N, int C, double *W)
 {

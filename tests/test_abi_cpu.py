@@ -31,6 +31,23 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_probe_library_exports_every_declared_function():
+    """include/moe_probe.h (measurement probes) against libmoeprobe.so."""
+    src = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_\w+)\(", src, re.M)))
+    assert names == ["moe_probe_empty_kernels", "moe_probe_stream_read"]
+    L = C.CDLL(os.path.join(ROOT, "bit_quantized_moe_block_amd", "libmoeprobe.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    # validation before any HIP call: misaligned size, null pointers, no blocks
+    L.moe_probe_stream_read.restype = C.c_int
+    L.moe_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p,
+                                        C.c_void_p]
+    assert L.moe_probe_stream_read(FAKE, 17, 4, FAKE, None) < 0
+    assert L.moe_probe_stream_read(None, 16, 4, FAKE, None) < 0
+    assert L.moe_probe_stream_read(FAKE, 16, 0, FAKE, None) < 0
+
+
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     assert int(re.search(r"MOE_DECODE_ABI_VERSION (\d+)u", src).group(1)) == B.MOE_DECODE_ABI_VERSION
