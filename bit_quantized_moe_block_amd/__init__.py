@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoedecode.so")
 
-MOE_DECODE_ABI_VERSION = 2
+MOE_DECODE_ABI_VERSION = 3
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_HIP, MOE_E_NOMEM, MOE_E_STREAM, MOE_E_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
 MOE_FMT_CODEBOOK, MOE_FMT_NVFP4 = 1, 2

@@ -594,17 +594,18 @@ __device__ __forceinline__ void load_group(GroupBuf<CLASS, NT> &b, const WaveJob
             b.w[i][0] = w0;
             b.w[i][1] = w1;
             b.w[i][2] = w2;
-            // scales[row][g], row = 16 trow + lane % 16
-            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, (trow * 16 * J.G + g) * 2, 0);
+            // the tile's 16 row scales are contiguous (tile order): lane
+            // offset 2 (lane % 16)
+            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, tile * 32, 0);
         } else {
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, tile * 1024, 0);
             b.w[i][0] = v[0];
             b.w[i][1] = v[1];
             b.w[i][2] = v[2];
             b.w[i][3] = v[3];
-            // scales[row][8 g + 2 (lane / 16) + {0, 1}]
-            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane,
-                                                           (J.rb0 + i) * 16 * (J.G * 8) + g * 8, 0);
+            // the tile's 16 x 8 block scales are contiguous (tile order, row
+            // major): lane offset 8 (lane % 16) + 2 (lane / 16)
+            b.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, tile * 128, 0);
         }
     }
 }
@@ -1183,7 +1184,7 @@ void expert_kernel(Params p)
             // 6-bit items: each row block takes two units of half the rows
             const int six = (has6<CLASS> && J.bits == 6) ? 1 : 0;
             const bool last = sb + 1 == (cur.half >= 0 ? 1 : cur.span << six);
-            const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+            const int sc_lane = is_cb<CLASS> ? r16 * 2 : r16 * 8 + 2 * q;
             // after the item's last row block comes the next item: its plan
             // entries (LDS) and descriptor (vector loads)
             const int nxt_ticket = ticket + (int)gridDim.x;
@@ -1677,7 +1678,7 @@ void prefill_kernel(Params p)
     J.G = DOWN ? p.I / 128 : p.H / 128;
     J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 7) * kPfNT;
     J.g0 = 0;
-    const int sc_lane = is_cb<CLASS> ? r16 * J.G * 2 : r16 * J.G * 8 + 2 * q;
+    const int sc_lane = is_cb<CLASS> ? r16 * 2 : r16 * 8 + 2 * q;
 
     // one MFMA subtile per 16 rows of the group: groups of up to 16 rows are
     // most experts at Zipf routing, 17 .. 48 rows the tails of hot experts

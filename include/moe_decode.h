@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 2u
+#define MOE_DECODE_ABI_VERSION 3u
 
 typedef struct moe_decode_s *moe_decode_t; /* opaque handle, owned by the library */
 
@@ -76,15 +76,19 @@ typedef enum { MOE_FMT_CODEBOOK = 1, MOE_FMT_NVFP4 = 2 } moe_format;
  *            words read as one 192-bit little-endian string; a 6-bit tile
  *            stores words 0..2 of its 64 slots (in slot order), then words
  *            3..5.
- *   scales : fp16, one per (row, 128-column group), row-major:
- *            scales[n*(C/128) + c/128]. 16-byte aligned.
+ *   scales : fp16, one per (row, 128-column group), stored per tile in the
+ *            tile order: the 16 scales of tile (rb, g) in row order,
+ *            scales[(rb*(C/128) + g)*16 + n%16] for row n = 16rb + n%16.
+ *            16-byte aligned.
  *   lut    : fp16[2^bits] codebook. W[n][c] = lut[code] * scale.
  *   tensor_scale: ignored.
  * MOE_FMT_NVFP4 (bits = 4): page "V100 換引擎", sections 4.0 and 7.1.
  *   codes  : bytes, 16 per slot; column jj in byte jj/2, low nibble for even jj
  *            (OCP e2m1). 16-byte aligned.
- *   scales : OCP e4m3fn bytes, one per (row, 16-column block), row-major:
- *            scales[n*(C/16) + c/16].
+ *   scales : OCP e4m3fn bytes, one per (row, 16-column block), stored per
+ *            tile in the tile order, a tile's 16 x 8 scales row-major:
+ *            scales[(rb*(C/128) + g)*128 + (n%16)*8 + (c%128)/16]. 16-byte
+ *            aligned.
  *   lut    : must be NULL.
  *   tensor_scale: fp32 host value, copied at create.
  *   W[n][c] = e2m1(code) * e4m3(scale) * tensor_scale.

@@ -225,14 +225,15 @@ uint32_t orc_codebook_code(int bits, int N, int C, const uint32_t *codes, int n,
     return code;
 }
 
-/* Group scales: fp16, one per (row, 128-column group), row-major:
- * scales[n * (C / 128) + c / 128]. */
+/* Group scales: fp16, one per (row, 128-column group), stored per 16 x 128
+ * tile in the tiles' order: the 16 scales of tile (n / 16, c / 128) in row
+ * order, i.e. scales[((n / 16) * (C / 128) + c / 128) * 16 + n % 16]. */
 double orc_codebook_weight(int bits, int N, int C, const uint32_t *codes, const uint16_t *scales,
                            const uint16_t *lut, int n, int c)
 {
     uint32_t code = orc_codebook_code(bits, N, C, codes, n, c);
     return orc_f16_to_double(lut[code]) *
-           orc_f16_to_double(scales[(long)n * (C / 128) + c / 128]);
+           orc_f16_to_double(scales[((long)(n / 16) * (C / 128) + c / 128) * 16 + n % 16]);
 }
 
 /* NVFP4: each slot is 16 bytes; column jj of the slot is the nibble of byte
@@ -248,12 +249,15 @@ uint8_t orc_nvfp4_code(int N, int C, const uint8_t *codes, int n, int c)
     return (jj % 2) ? (byte >> 4) : (byte & 0xF);
 }
 
-/* NVFP4 block scales: e4m3fn, one per (row, 16-column block), row-major:
- * scales[n * (C / 16) + c / 16]. W = e2m1(code) * e4m3(scale) * tensor_scale. */
+/* NVFP4 block scales: e4m3fn, one per (row, 16-column block), stored per
+ * 16 x 128 tile in the tiles' order, each tile's 16 x 8 scales row-major:
+ * scales[((n / 16) * (C / 128) + c / 128) * 128 + (n % 16) * 8 + (c % 128) / 16].
+ * W = e2m1(code) * e4m3(scale) * tensor_scale. */
 double orc_nvfp4_weight(int N, int C, const uint8_t *codes, const uint8_t *scales, float ts, int n,
                         int c)
 {
-    double s = orc_e4m3fn_to_double(scales[(long)n * (C / 16) + c / 16]);
+    double s = orc_e4m3fn_to_double(
+        scales[((long)(n / 16) * (C / 128) + c / 128) * 128 + (n % 16) * 8 + (c % 128) / 16]);
     return orc_e2m1_to_double(orc_nvfp4_code(N, C, codes, n, c)) * s * (double)ts;
 }
 

@@ -127,8 +127,17 @@ def pack_codebook(codes, bits):
 
 
 def codebook_scales(scales, N, C):
-    """Scale matrix [N, C // 128] (fp64) from row-major fp16 scales."""
-    return np.asarray(scales, np.float16).astype(np.float64).reshape(N, C // 128)
+    """Scale matrix [N, C // 128] (fp64) from the stored fp16 scales: per
+    16 x 128 tile (tile order), the tile's 16 row scales."""
+    RB, G = N // 16, C // 128
+    s = np.asarray(scales, np.float16).astype(np.float64).reshape(RB, G, 16)
+    return s.transpose(0, 2, 1).reshape(N, G)
+
+
+def pack_codebook_scales(sc):
+    """Stored order of a scale matrix [N, C // 128]."""
+    N, G = sc.shape
+    return np.ascontiguousarray(sc.reshape(N // 16, 16, G).transpose(0, 2, 1)).reshape(-1)
 
 
 def dense_codebook(t, N, C):
@@ -147,7 +156,9 @@ def nvfp4_codes(codes, N, C):
 def dense_nvfp4(t, N, C):
     RB, G = N // 16, C // 128
     vals = E2M1_VALUES[nvfp4_codes(t["codes"], N, C)]
-    sc = e4m3fn_table()[np.asarray(t["scales"], np.uint8)].reshape(N, C // 16)
+    # stored per 16 x 128 tile (tile order), a tile's 16 x 8 scales row-major
+    sc = e4m3fn_table()[np.asarray(t["scales"], np.uint8)].reshape(RB, G, 16, 8)
+    sc = sc.transpose(0, 2, 1, 3).reshape(N, C // 16)
     return vals * np.repeat(sc, 16, axis=1) * float(np.float32(t["tensor_scale"]))
 
 

@@ -33,8 +33,11 @@ MUTANTS = [
     ("6-bit tile not split", "tau * 384 + (word[k] / 3) * 192 + slot * 3 + word[k] % 3",
      "tau * 384 + slot * 6 + word[k]"),
     ("slot transposed", "int slot = q * 16 + r;", "int slot = r * 4 + q;"),
-    ("group scale column-major", "orc_f16_to_double(scales[(long)n * (C / 128) + c / 128]);",
-     "orc_f16_to_double(scales[(long)(c / 128) * N + n]);"),
+    ("group scale row-major", "orc_f16_to_double(scales[((long)(n / 16) * (C / 128) + c / 128) * 16 + n % 16]);",
+     "orc_f16_to_double(scales[(long)n * (C / 128) + c / 128]);"),
+    ("NVFP4 block scale row-major",
+     "scales[((long)(n / 16) * (C / 128) + c / 128) * 128 + (n % 16) * 8 + (c % 128) / 16]);",
+     "scales[(long)n * (C / 16) + c / 16]);"),
     ("NVFP4 nibble order", "return (jj % 2) ? (byte >> 4) : (byte & 0xF);",
      "return (jj % 2) ? (byte & 0xF) : (byte >> 4);"),
     ("top-k ties to the higher id", "if (best < 0 || l[e] > l[best])", "if (best < 0 || l[e] >= l[best])"),

@@ -184,7 +184,7 @@ def test_codebook_roundtrip_exact_weights(bits):
     assert np.array_equal(enc, codes)
     words = brute.pack_codebook(enc, bits)
     L = oracle.Layer("codebook", 1, 1, C, N, [bits],
-                     {(0, 0): dict(codes=words, scales=sc.reshape(-1), lut=lut)})
+                     {(0, 0): dict(codes=words, scales=brute.pack_codebook_scales(sc), lut=lut)})
     assert np.array_equal(L.dequant(0, 0), W)
 
 
