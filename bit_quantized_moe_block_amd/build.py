@@ -18,6 +18,9 @@ FLAGS = [
     # Packed-fp32 VALU forms stay off (only scalar / MFMA fp32 arithmetic).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    # leading scalar kernel arguments arrive in scalar registers at launch
+    # (the route and combine kernels put theirs first)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

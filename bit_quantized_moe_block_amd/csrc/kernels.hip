@@ -197,10 +197,11 @@ __device__ __forceinline__ int ld_coherent_i32(const int32_t *p)
 // reduction); lane j keeps slot j. Weights: softmax over the k selected
 // logits, the denominator summed in slot order. ids go out agent-coherent for
 // the bucketing block, and to s_ids (if given) for a bucketing in this block.
-__device__ void route_token(const Params &p, const float *__restrict__ logits, int t, int *s_ids)
+__device__ void route_token(const Params &p, const float *__restrict__ logits, int E, int t,
+                            int *s_ids)
 {
     const int lane = threadIdx.x & 63;
-    const int E = p.E, k = p.k;
+    const int k = p.k;
     uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -358,10 +359,12 @@ __device__ void bucket_block(const Params &p, int m, const int *s_ids)
 // 16 waves, one block for 16 tokens, measured slower at m = 16: four top-k
 // waves per SIMD instead of one.) The remaining blocks: one wave per (token, 128-column
 // block) rotates x (codebook) or converts it to fp16 (NVFP4).
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
+// The scalar arguments come first: the kernel-argument preload puts them in
+// scalar registers at launch, so the logit loads need not wait for the
+// parameter block's loads (E is also in p; this copy is the preloaded one).
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits,
                                                               const uint16_t *__restrict__ x,
-                                                              const float *__restrict__ logits,
-                                                              int m)
+                                                              int m, int E, Params p)
 {
     __shared__ int s_last;
     __shared__ int s_ids[kRouteWaves * kMaxTopK];
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
     const int wave = threadIdx.x >> 6;
     if (nk == 1 && blockIdx.x == 0) {
         if (wave < m)
-            route_token(p, logits, wave, s_ids);
+            route_token(p, logits, E, wave, s_ids);
         __syncthreads();
         bucket_block(p, m, s_ids);
         return;
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(Params p,
     if ((int)blockIdx.x < nk) {
         const int t = blockIdx.x * kRouteWaves + wave;
         if (t < m)
-            route_token(p, logits, t, nullptr);
+            route_token(p, logits, E, t, nullptr);
         wait_stores();
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -1285,77 +1288,68 @@ void expert_kernel(Params p)
 // the shared expert's row (weight 1) when there is one. Block
 // (rb, t) covers rows rb*256 .. +255 of token t; runs after the expert
 // kernel, so plain loads see its partial sums.
-__global__ __launch_bounds__(64) void combine_kernel(Params p)
+// One round of loads: every slot's weight and partial sums of the first two
+// splits, the shared expert's row and the error word are issued before any
+// is used (further splits, where a layer has more than two, follow in a
+// second round); then the sums, in the order above. Every load is issued
+// whatever k and the split count (indices past them are clamped to the last
+// slot / split and their values not used), so that the compiler can keep
+// them all in flight. KMAX: 8 or 16 slots. The scalar arguments come first:
+// the kernel-argument preload puts them in scalar registers at launch, so
+// the loads need not wait for the parameter block (they are also in p).
+template <int KMAX>
+__global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ y_part,
+                                                     const float *__restrict__ wts,
+                                                     const Counters *ctr, int k, int ks2,
+                                                     int pair_cap, int H, int has_shared, Params p)
 {
-    // one wave per (256-row block, token); lane l owns rows 4l .. 4l+3 of the
-    // block and moves them as 16-byte loads and stores
     const int t = blockIdx.y, row = blockIdx.x * 256 + 4 * threadIdx.x;
-    constexpr int SPP = 4;  // slots per pass
-    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < p.k; j0 += SPP) {
-        int pp[SPP];
-        float wj[SPP];
+    const bool shared = has_shared != 0;
+    const uint32_t err = ctr->error_word;
+    const int s1 = ks2 > 1 ? 1 : 0;
+    auto part = [&](int s, size_t q) { return *(const floatx4 *)(y_part + ((size_t)s * pair_cap + q) * H + row); };
+    float wj[KMAX];
+    floatx4 v[KMAX][2];
 #pragma unroll
-        for (int jj = 0; jj < SPP; ++jj) {
-            pp[jj] = 0;
-            wj[jj] = 0.0f;
-            if (j0 + jj < p.k) {
-                pp[jj] = t * p.k + j0 + jj;  // partials are stored by pair index
-                wj[jj] = p.wts[t * p.k + j0 + jj];
-            }
-        }
-        floatx4 y[SPP];
-#pragma unroll
-        for (int jj = 0; jj < SPP; ++jj)
-            y[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < p.ks2; s0 += 2) {
-            floatx4 v[SPP][2];
-#pragma unroll
-            for (int jj = 0; jj < SPP; ++jj)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    v[jj][s] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    if (j0 + jj < p.k && s0 + s < p.ks2)
-                        v[jj][s] = *(const floatx4 *)(p.y_part +
-                                                      ((size_t)(s0 + s) * p.pair_cap + pp[jj]) * p.H + row);
-                }
-#pragma unroll
-            for (int jj = 0; jj < SPP; ++jj)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    if (s0 + s < p.ks2)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            y[jj][c] += v[jj][s][c];
-        }
-#pragma unroll
-        for (int jj = 0; jj < SPP; ++jj)
-            if (j0 + jj < p.k)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    o[c] += wj[jj] * y[jj][c];
+    for (int j = 0; j < KMAX; ++j) {
+        const size_t q = (size_t)t * k + min(j, k - 1);  // partials are stored by pair index
+        wj[j] = wts[q];
+        v[j][0] = part(0, q);
+        v[j][1] = part(s1, q);
     }
-    if (p.has_shared) {
-        // the shared expert's row of token t (bucket row m*k + t), weight 1,
-        // after the routed slots
-        const size_t q = (size_t)gridDim.y * p.k + t;
-        floatx4 ysh = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < p.ks2; ++s) {
-            const floatx4 v = *(const floatx4 *)(p.y_part + ((size_t)s * p.pair_cap + q) * p.H + row);
+    // the shared expert's row of token t: bucket row m*k + t (a routed row
+    // when there is no shared expert: loaded, not used)
+    const size_t qsh = shared ? (size_t)gridDim.y * k + t : (size_t)t * k;
+    const floatx4 vsh0 = part(0, qsh), vsh1 = part(s1, qsh);
+    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                ysh[c] += v[c];
-        }
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k)
+            break;
+        floatx4 y = v[j][0];
+        if (ks2 > 1)
+            y += v[j][1];
+        for (int s = 2; s < ks2; ++s)
+            y += part(s, (size_t)t * k + j);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            o[c] += ysh[c];
+            o[c] += wj[j] * y[c];
+    }
+    if (shared) {
+        // weight 1, after the routed slots
+        floatx4 ysh = vsh0;
+        if (ks2 > 1)
+            ysh += vsh1;
+        for (int s = 2; s < ks2; ++s)
+            ysh += part(s, qsh);
+        o += ysh;
     }
     // a dependency wait of the expert kernel gave up (some down partial
     // sums are stale): the failure shows in the output instead of a
     // plausible wrong value
-    if (__builtin_amdgcn_readfirstlane(*(volatile uint32_t *)&p.ctr->error_word) != 0u)
+    if (__builtin_amdgcn_readfirstlane(err) != 0u)
         o = floatx4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    *(floatx4 *)(p.out + (size_t)t * p.H + row) = o;
+    *(floatx4 *)(p.out + (size_t)t * H + row) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -1703,7 +1697,7 @@ hipError_t launch_route(const Params &p, const uint16_t *x, const float *logits,
 {
     const int tasks = m * (p.H / 128);
     const int blocks = (m + kRouteWaves - 1) / kRouteWaves + (tasks + kRouteWaves - 1) / kRouteWaves;
-    route_kernel<<<dim3(blocks), dim3(kRouteThreads), route_lds_bytes(p.E, m), s>>>(p, x, logits, m);
+    route_kernel<<<dim3(blocks), dim3(kRouteThreads), route_lds_bytes(p.E, m), s>>>(logits, x, m, p.E, p);
     return hipGetLastError();
 }
 
@@ -1759,7 +1753,12 @@ hipError_t launch_prefill(const Params &p, int grid_groups, hipStream_t s)
 
 hipError_t launch_combine(const Params &p, int m, hipStream_t s)
 {
-    combine_kernel<<<dim3(p.n_rb2, m), dim3(64), 0, s>>>(p);
+    if (p.k <= 8)
+        combine_kernel<8><<<dim3(p.n_rb2, m), dim3(64), 0, s>>>(p.y_part, p.wts, p.ctr, p.k, p.ks2,
+                                                                p.pair_cap, p.H, p.has_shared, p);
+    else
+        combine_kernel<kMaxTopK><<<dim3(p.n_rb2, m), dim3(64), 0, s>>>(
+            p.y_part, p.wts, p.ctr, p.k, p.ks2, p.pair_cap, p.H, p.has_shared, p);
     return hipGetLastError();
 }
 
