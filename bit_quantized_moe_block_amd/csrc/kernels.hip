@@ -202,12 +202,16 @@ __device__ void route_token(const Params &p, const float *__restrict__ logits, i
 {
     const int lane = threadIdx.x & 63;
     const int k = p.k;
+    // the four loads are issued together (an expert index past E is clamped
+    // and its key dropped afterwards), not one at a time under the condition
+    float lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        lv[i] = logits[(size_t)t * E + min(lane + 64 * i, E - 1)];
     uint32_t key[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? float_key(logits[(size_t)t * E + e]) : 0u;
-    }
+    for (int i = 0; i < 4; ++i)
+        key[i] = lane + 64 * i < E ? float_key(lv[i]) : 0u;
     int my_id = 0;
     uint32_t my_key = 0;
     for (int j = 0; j < k; ++j) {
@@ -403,8 +407,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
     const uint32_t xx = *(const uint32_t *)(x + (size_t)t * p.H + c0);
     float v0 = bf16_to_f32(xx & 0xFFFFu), v1 = bf16_to_f32(xx >> 16);
     if (p.format == kFmtCodebook) {
-        v0 *= (float)p.signs_h[c0];
-        v1 *= (float)p.signs_h[c0 + 1];
+        // the two signs in one 16-bit load, issued before x is used
+        const uint16_t sg = *(const uint16_t *)(p.signs_h + c0);
+        v0 *= (float)(int8_t)(sg & 0xFF);
+        v1 *= (float)(int8_t)(sg >> 8);
         wave_fwht128(v0, v1);
         v0 *= kInvSqrt128;
         v1 *= kInvSqrt128;
