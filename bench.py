@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the plain-read and launch-floor probes")
     ap.add_argument("--profile-passes", type=int, default=3)
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only run the LDS read probe over the three staging layouts and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device once (the known-size dispatch "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -157,6 +159,9 @@ def probe_lib():
                                             C.c_void_p]
         L.moe_probe_empty_kernels.restype = C.c_int
         L.moe_probe_empty_kernels.argtypes = [C.c_int32, C.c_void_p]
+        L.moe_probe_lds_read128.restype = C.c_int
+        L.moe_probe_lds_read128.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                            C.c_void_p]
         _probe = L
     return _probe
 
@@ -186,6 +191,34 @@ def probe_plain_read(dev, gib=4, reps=5):
                 best, best_grid = t, grid
     del buf
     return nbytes / (best * 1e-3) / 1e9, best_grid
+
+
+LDS_LAYOUTS = ("rows padded by 16 bytes (decode kernel)", "256-byte rows, xor-permuted pieces (prefill)",
+               "256-byte rows, unpadded (conflicted reference)")
+
+
+def probe_lds_layouts(dev, blocks=1024, iters=256):
+    """LDS read rate of the MFMA activation-operand pattern per staging layout:
+    one launch per layout (in LDS_LAYOUTS order) after one warm-up launch each.
+    Returns [(layout, us, clocks per 16-byte read per CU at 2.4 GHz)]."""
+    import torch
+    L = probe_lib()
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reads_per_cu = blocks * 4 * iters * 16 / torch.cuda.get_device_properties(dev).multi_processor_count
+    out = []
+    for layout in range(len(LDS_LAYOUTS)):
+        for timed in (False, True):
+            e0.record(s)
+            rc = L.moe_probe_lds_read128(layout, blocks, iters, sink.data_ptr(), s.cuda_stream)
+            e1.record(s)
+            if rc:
+                raise RuntimeError(f"moe_probe_lds_read128: HIP error {-rc}")
+            e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        out.append((layout, us, us * 1e-6 * 2.4e9 / reads_per_cu))
+    return out
 
 
 def probe_launch_floor(dev, layers, reps=50):
@@ -230,6 +263,15 @@ def main():
     import numpy as np
     import torch
 
+    if args.lds_probe:
+        res = probe_lds_layouts(torch.device("cuda", 0))
+        for layout, us, clk in res:
+            log(f"lds probe layout {layout} ({LDS_LAYOUTS[layout]}): {us:.1f} us, "
+                f"{clk:.2f} clocks per 16-byte read per CU")
+        print(json.dumps({"lds_probe": [{"layout": l, "desc": LDS_LAYOUTS[l], "us": round(us, 1),
+                                         "clocks_per_read_per_cu": round(c, 3)}
+                                        for l, us, c in res]}))
+        return
     if args.copy_calibration:
         n = args.copy_calibration << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -1314,32 +1314,41 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ y
     const uint32_t err = ctr->error_word;
     const int s1 = ks2 > 1 ? 1 : 0;
     auto part = [&](int s, size_t q) { return *(const floatx4 *)(y_part + ((size_t)s * pair_cap + q) * H + row); };
-    float wj[KMAX];
-    floatx4 v[KMAX][2];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        const size_t q = (size_t)t * k + min(j, k - 1);  // partials are stored by pair index
-        wj[j] = wts[q];
-        v[j][0] = part(0, q);
-        v[j][1] = part(s1, q);
-    }
     // the shared expert's row of token t: bucket row m*k + t (a routed row
     // when there is no shared expert: loaded, not used)
     const size_t qsh = shared ? (size_t)gridDim.y * k + t : (size_t)t * k;
     const floatx4 vsh0 = part(0, qsh), vsh1 = part(s1, qsh);
     floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+    // slots in rounds of up to 8: one round's loads all issue before its sums;
+    // a 16-slot round's arrays would be too large to stay in registers
+    constexpr int CH = KMAX < 8 ? KMAX : 8;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        if (j >= k)
+    for (int j0 = 0; j0 < KMAX; j0 += CH) {
+        if (j0 >= k)
             break;
-        floatx4 y = v[j][0];
-        if (ks2 > 1)
-            y += v[j][1];
-        for (int s = 2; s < ks2; ++s)
-            y += part(s, (size_t)t * k + j);
+        float wj[CH];
+        floatx4 v[CH][2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            o[c] += wj[j] * y[c];
+        for (int jj = 0; jj < CH; ++jj) {
+            const size_t q = (size_t)t * k + min(j0 + jj, k - 1);  // partials are stored by pair index
+            wj[jj] = wts[q];
+            v[jj][0] = part(0, q);
+            v[jj][1] = part(s1, q);
+        }
+#pragma unroll
+        for (int jj = 0; jj < CH; ++jj) {
+            const int j = j0 + jj;
+            if (j >= k)
+                break;
+            floatx4 y = v[jj][0];
+            if (ks2 > 1)
+                y += v[jj][1];
+            for (int s = 2; s < ks2; ++s)
+                y += part(s, (size_t)t * k + j);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                o[c] += wj[jj] * y[c];
+        }
     }
     if (shared) {
         // weight 1, after the routed slots
@@ -1365,26 +1374,34 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ y
 // cut into row groups of up to 64 rows, and each decoded weight step feeds
 // one MFMA per 16-row subtile of the group (up to four): the decode, the VALU
 // cost of these formats, is paid once per 64 rows instead of once per 16. A block
-// covers one row group and 128 output rows (of gate and of up: eight waves
-// of one 16-row tile each) or 256 (down: sixteen waves), over all input
+// covers one row group and 128 output rows (of gate and of up: four waves
+// of two 16-row tiles each) or 256 (down: eight waves), over all input
 // columns, so there are no column splits
 // and no partial sums. The gate/up block finishes SiLU(g) u and the h
 // rotation of its 128 rows itself (exactly one rotation block); the down
 // block writes y; the combine kernel sums the slots. The down kernel runs
 // after the gate/up kernel in stream order.
 
-constexpr int kPfThreads = 1024;                  // 16 waves: 8 per projection (gate/up)
+constexpr int kPfThreads = 512;                   // 8 waves: 4 per projection (gate/up)
 constexpr int kPfWaves = kPfThreads / 64;
-constexpr int kPfNT = 1;                          // 16-row tiles per wave
+constexpr int kPfNT = 2;                          // 16-row tiles per wave
+constexpr int kPfProjWaves = 8 / kPfNT;           // gate/up: waves per projection (128 rows)
 constexpr int kPfRows = 64;                       // rows of a prefill row group
 constexpr int kPfSub = kPfRows / 16;              // MFMA subtiles per row group
-constexpr int kPfAStride = 128 + kLdsPadHalves;   // staged chunk row stride (halves)
+// Staged chunk rows are 256 bytes (128 halves) unpadded; the 16-byte piece p
+// of row r sits at piece p ^ (r mod 16) of its row, so that the 16 rows one
+// MFMA operand read spans (row r16 of lane r16, pieces 4q + s) and the 16
+// pieces one row's staging write covers each fall on distinct LDS banks.
+constexpr int kPfAStride = 128;                   // staged chunk row stride (halves)
 constexpr int kPfHStride = 128 + 4;               // epilogue buffer row stride (floats)
-constexpr size_t kPfLds = 2 * kPfRows * kPfAStride * sizeof(_Float16);
+constexpr size_t kPfLds = 2 * kPfRows * kPfAStride * sizeof(_Float16) > kPfRows * kPfHStride * sizeof(float)
+                              ? 2 * kPfRows * kPfAStride * sizeof(_Float16)
+                              : kPfRows * kPfHStride * sizeof(float);
+__device__ __forceinline__ int pf_piece(int row, int piece) { return row * kPfAStride + ((piece ^ row) & 15) * 8; }
 
 // One 128-column chunk of the first ROWS activation rows of the group (the
 // rows of its NSUB subtiles, ROWS = 16 NSUB): ROWS x 128 fp16 = 16 ROWS
-// 16-byte pieces, piece i by thread i mod 1024; rows past R repeat row R-1
+// 16-byte pieces, piece i by thread i mod 512; rows past R repeat row R-1
 // (their results are never stored). A piece index past the end skips whole
 // waves (256 pieces = 4 waves). Gate/up rows are tokens: lane r of every
 // wave holds the token of row r. Down rows off .. off+R-1 of h~ are
@@ -1426,7 +1443,7 @@ struct PfStage {
             const int i = tid + k * kPfThreads;
             if (PIECES % kPfThreads != 0 && i >= PIECES)
                 continue;
-            *(u32x4 *)(A + (i >> 4) * kPfAStride + (i & 15) * 8) = v[k];
+            *(u32x4 *)(A + pf_piece(i >> 4, i & 15)) = v[k];
         }
     }
 };
@@ -1443,9 +1460,10 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t w, _Float16 f)
 // staged 16-row subtiles (A, B and result layouts as in process_group;
 // subtile t = rows 16t .. 16t+15; NSUB = ceil(R / 16), fixed per loop
 // instance: per-subtile branches inside the loop cost more issue slots than
-// the MFMAs they skip). Per step: the subtiles' A operands, then per tile one
-// decode and NSUB MFMAs; staged rows past R repeat row R-1 and their results
-// are never stored. Codebook: the group's MFMA sums are scaled by the fp16
+// the MFMAs they skip). Per step: one decode per tile, then per subtile its A
+// operand and one MFMA per tile (each A operand read from LDS feeds kPfNT
+// MFMAs); staged rows past R repeat row R-1 and their results are never
+// stored. Codebook: the group's MFMA sums are scaled by the fp16
 // group scale in fp32 and added to the accumulators, as in the decode kernel
 // (the scaled weight is never rounded). NVFP4: the e4m3 block scale is exact
 // in the fp16 operand, so the MFMAs accumulate directly.
@@ -1463,10 +1481,7 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
                 cc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        half8 a[NSUB];
-#pragma unroll
-        for (int t = 0; t < NSUB; ++t)
-            a[t] = *(const half8 *)(A + (16 * t + r16) * kPfAStride + q * 32 + s * 8);
+        half8 bv[kPfNT];
 #pragma unroll
         for (int i = 0; i < kPfNT; ++i) {
             half2v bs = half2v{1, 1};
@@ -1475,13 +1490,17 @@ __device__ __forceinline__ void pf_group(const GroupBuf<CLASS, kPfNT> &b, const 
                                                     : __builtin_amdgcn_cvt_f32_fp8(b.sc[i], 1));
                 bs = half2v{v, v};
             }
-            const half8 bv = decode_step<FMT>(b.w[i], s, tab, bs);
+            bv[i] = decode_step<FMT>(b.w[i], s, tab, bs);
+        }
 #pragma unroll
-            for (int t = 0; t < NSUB; ++t) {
+        for (int t = 0; t < NSUB; ++t) {
+            const half8 a = *(const half8 *)(A + pf_piece(16 * t + r16, 4 * q + s));
+#pragma unroll
+            for (int i = 0; i < kPfNT; ++i) {
                 if constexpr (FMT == 4)
-                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, acc[i][t], 0, 0, 0);
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv[i], acc[i][t], 0, 0, 0);
                 else
-                    cc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bv, cc[i][t], 0, 0, 0);
+                    cc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv[i], cc[i][t], 0, 0, 0);
             }
         }
     }
@@ -1585,10 +1604,10 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
                 }
     } else {
         // h = silu(g) u through LDS (the up waves' u, then the gate waves'
-        // h in place), then each wave rotates the h of rows wave, wave + 16, ...
+        // h in place), then each wave rotates the h of rows wave, wave + 8, ...
         float *hb = (float *)pf_lds;  // [64 rows][kPfHStride]
-        const int lr0 = (wave & 7) * (kPfNT * 16);
-        if (wave >= 8)
+        const int lr0 = (wave % kPfProjWaves) * (kPfNT * 16);
+        if (wave >= kPfProjWaves)
 #pragma unroll
             for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
@@ -1600,7 +1619,7 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
                             hb[row * kPfHStride + lr0 + 16 * i + r16] = acc[i][t][j];
                     }
         __syncthreads();
-        if (wave < 8)
+        if (wave < kPfProjWaves)
 #pragma unroll
             for (int i = 0; i < kPfNT; ++i)
 #pragma unroll
@@ -1649,6 +1668,8 @@ __device__ __forceinline__ void pf_dispatch(const Params &p, _Float16 *pf_lds, c
 // groups through two register buffers: chunk c+1's activations and weight
 // group c+2 load while chunk c is computed.
 template <int CLASS, bool DOWN>
+// two blocks per CU (four waves per SIMD, at most 128 VGPRs): one block's
+// barrier waits are covered by the other block's work
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_kernel(Params p)
 {
@@ -1668,7 +1689,7 @@ void prefill_kernel(Params p)
         const int qrow = off + min(lane, R - 1);
         tok = qrow < m * p.k ? p.rows[qrow] / p.k : qrow - m * p.k;
     }
-    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave >> 3)];
+    const DevTensor d = p.tensors[e * 3 + (DOWN ? 2 : wave / kPfProjWaves)];
     WaveJob J;
     J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
     J.scales = (gu8p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.scales);
@@ -1676,7 +1697,7 @@ void prefill_kernel(Params p)
     J.ts = __uint_as_float((uint32_t)uniform((int)__float_as_uint(d.tensor_scale)));
     J.bits = uniform(d.bits);
     J.G = DOWN ? p.I / 128 : p.H / 128;
-    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave & 7) * kPfNT;
+    J.rb0 = DOWN ? rb * 16 + wave * kPfNT : rb * 8 + (wave % kPfProjWaves) * kPfNT;
     J.g0 = 0;
     const int sc_lane = is_cb<CLASS> ? r16 * 2 : r16 * 8 + 2 * q;
 

@@ -1,6 +1,6 @@
 // Measurement probes (include/moe_probe.h): a plain streaming read of a
-// device buffer and an empty kernel. Nothing of the decode step is computed
-// here.
+// device buffer, an empty kernel and the LDS read pattern of the MFMA
+// activation operands. Nothing of the decode step is computed here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +31,52 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4 *__restrict__ buf
 
 __global__ void empty_kernel() {}
 
+// The activation-operand reads of a 16x16x32 MFMA over four 16-row
+// subtiles of staged fp16 rows: lane (r = lane % 16, q = lane / 16) reads the
+// 16-byte piece 4q + s of row 16t + r, for steps s = 0..3 and subtiles
+// t = 0..3, `iters` times. Layout 0: rows of 272 bytes (128 halves and 16
+// bytes of padding); 1: rows of 256 bytes, piece p of row r stored at piece
+// p ^ (r mod 16); 2: rows of 256 bytes, no padding (the 16 rows of one read
+// start on the same bank).
+constexpr int kLdsRows = 64, kLdsStride = 136;  // halves
+
+__device__ __forceinline__ int lds_probe_offset(int layout, int row, int piece)
+{
+    if (layout == 0)
+        return row * kLdsStride + piece * 8;
+    if (layout == 1)
+        return row * 128 + ((piece ^ row) & 15) * 8;
+    return row * 128 + piece * 8;
+}
+
+__global__ __launch_bounds__(256) void lds_read128(int layout, int iters, uint32_t *sink)
+{
+    __shared__ __align__(16) uint16_t A[kLdsRows * kLdsStride];
+    for (int i = threadIdx.x; i < kLdsRows * kLdsStride; i += 256)
+        A[i] = (uint16_t)(i * 40503u);
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    int off[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            off[4 * t + s] = lds_probe_offset(layout, 16 * t + r, 4 * q + s);
+    // the offsets are loop-invariant; xor-ing in (it & zero), zero = 0 at run
+    // time, keeps every read inside the loop
+    const int zero = iters >> 30;
+    u32x4 acc = u32x4{0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        const int z = it & zero;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            acc ^= *(const u32x4 *)(A + (off[k] ^ z));
+    }
+    const uint32_t f = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (f == 0x9E3779B9u)
+        sink[0] = f;
+}
+
 }  // namespace
 
 extern "C" int moe_probe_stream_read(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink,
@@ -52,4 +98,13 @@ extern "C" int moe_probe_empty_kernels(int32_t count, void *hip_stream)
             return -(int)e;
     }
     return 0;
+}
+
+extern "C" int moe_probe_lds_read128(int32_t layout, int32_t blocks, int32_t iters, uint32_t *sink,
+                                     void *hip_stream)
+{
+    if (layout < 0 || layout > 2 || blocks < 1 || iters < 1 || iters >= (1 << 30) || !sink)
+        return -(int)hipErrorInvalidValue;
+    lds_read128<<<dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream>>>(layout, iters, sink);
+    return -(int)hipGetLastError();
 }

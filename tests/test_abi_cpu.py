@@ -35,7 +35,7 @@ def test_probe_library_exports_every_declared_function():
     """include/moe_probe.h (measurement probes) against libmoeprobe.so."""
     src = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_\w+)\(", src, re.M)))
-    assert names == ["moe_probe_empty_kernels", "moe_probe_stream_read"]
+    assert names == ["moe_probe_empty_kernels", "moe_probe_lds_read128", "moe_probe_stream_read"]
     L = C.CDLL(os.path.join(ROOT, "bit_quantized_moe_block_amd", "libmoeprobe.so"))
     for n in names:
         assert hasattr(L, n), n
