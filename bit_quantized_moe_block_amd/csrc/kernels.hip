@@ -977,14 +977,16 @@ __device__ void finish_h(const Params &p, int off, int R, int rb)
     }
 }
 
-// Wait until every 128-row block of h~ of row group u is written (bounded).
-// The pause between polls doubles up to about a microsecond, so waiting
-// blocks add little traffic to the counter the producers increment.
-__device__ __forceinline__ bool wait_h(const Params &p, int u)
+// Wait until row group u's h counter reaches `target` (bounded): every
+// 128-row block of h~ written (persistent kernel), or every gate/up item of
+// the group counted (small-m kernel). The pause between polls doubles up to
+// about a microsecond, so waiting blocks add little traffic to the counter
+// the producers increment.
+__device__ __forceinline__ bool wait_h(const Params &p, int u, uint32_t target)
 {
     uint32_t polls = 0;
     int pause = 1;
-    while (atomic_load_agent(&p.h_ready[u * kCtrStride]) < (uint32_t)p.n_rb1) {
+    while (atomic_load_agent(&p.h_ready[u * kCtrStride]) < target) {
         for (int i = 0; i < pause; ++i)
             __builtin_amdgcn_s_sleep(4);
         pause = min(2 * pause, 8);
@@ -1153,7 +1155,7 @@ template <int CLASS, int NG>
 __global__ __launch_bounds__(kExpertThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void expert_kernel(Params p)
 {
-    extern __shared__ _Float16 Abuf[];  // min(m, 16) staged rows, then the row-group table
+    extern __shared__ __align__(16) _Float16 Abuf[];  // min(m, 16) staged rows, then the row-group table
     __shared__ Smem sm;
     using St = Stage<NG>;
     const Plan *P = p.plan;
@@ -1223,7 +1225,7 @@ void expert_kernel(Params p)
                 if (cur.down) {
                     __builtin_amdgcn_s_setprio(0);  // waiting yields to the others
                     if (tid == 0)
-                        sm.flag = wait_h(p, cur.u);
+                        sm.flag = wait_h(p, cur.u, (uint32_t)p.n_rb1);
                     __syncthreads();
                     ok = sm.flag != 0;
                 }
@@ -1286,6 +1288,323 @@ void expert_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Small-m kernel (up to kSmallMaxTokens tokens): items by rows, all columns
+// ---------------------------------------------------------------------------
+// With one to four tokens the persistent kernel's column splits leave part of
+// the grid idle and put a round trip between gate/up and down (partial sums,
+// a split counter, the finishing block, the h counter). Here a gate/up item is
+// 32 rows of gate and of up over all H columns (waves 0-1 gate, 2-3 up, one
+// 16-row tile each): its sums are whole, so the item applies SiLU(g) u itself
+// and stores h for its rows (fp32, not yet rotated), then counts on its row
+// group's h counter. A down item is 64 rows of down over all I columns (one
+// tile per wave): it loads its first kSmDepth weight groups, waits until
+// every gate/up item of its group has counted, rotates h~ from h (one wave per
+// token and 128-column block: the same fp32 arithmetic as the persistent
+// kernel's finishing block), and writes y whole (one split). A wave streams
+// its tile through kSmDepth register buffers, so a waiting down item already
+// has its first groups in flight. Tickets: the gate/up items of every row
+// group, then the down items; block b takes b, b + G, ... in order (no wait
+// can deadlock, as in the persistent kernel). Plan, buckets, combine: shared
+// with the persistent kernel.
+constexpr int kSmGuRows = 32;      // rows of gate and of up per gate/up item
+constexpr int kSmDnRows = 64;      // rows of down per down item
+constexpr int kSmDepth = 8;        // weight groups in flight per wave
+constexpr int kSmStageIters = 8;   // 16-byte staging loads per thread (R x H <= 16384)
+constexpr int kSmRotBatch = 4;     // h loads a wave issues together when rotating
+
+// Group j of one 16-row tile (buffer b) against the staged rows: as
+// process_group, for one tile.
+template <int CLASS, int FMT>
+__device__ __forceinline__ void sm_group(const GroupBuf<CLASS, 1> &b, const _Float16 *Ag,
+                                         const uint32_t (&tab)[4], floatx4 &acc)
+{
+    half8 a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a[s] = *(const half8 *)(Ag + s * 8);
+    half2v bs_lo = half2v{1, 1}, bs_hi = half2v{1, 1};
+    if constexpr (FMT == 4) {
+        const _Float16 lo = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.sc[0], 0);
+        const _Float16 hi = (_Float16)__builtin_amdgcn_cvt_f32_fp8(b.sc[0], 1);
+        bs_lo = half2v{lo, lo};
+        bs_hi = half2v{hi, hi};
+    }
+    floatx4 cc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            a[s], decode_step<FMT>(b.w[0], s, tab, s < 2 ? bs_lo : bs_hi), cc, 0, 0, 0);
+    if constexpr (FMT == 4) {
+        acc += cc;
+    } else {
+        const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[0]);
+        acc += f * cc;
+    }
+    asm volatile("" : "+v"(acc));
+}
+
+// The wave's tile stream: group g of its tile row is tile t = rb0 * G + g of
+// the tensor. Codebook tiles of either width load as one 12-byte load per
+// lane at lane offset 8 (2-bit) or 12 (3-bit) bytes, through a buffer
+// resource sized to the tensor (the 4 bytes a 2-bit lane reads past its own
+// are not used; past the tensor's end they read as zero), so that 2- and
+// 3-bit tiles issue the same instruction and the waits placed for the loads
+// stay exact whichever width a wave has.
+template <int CLASS>
+struct SmTiles {
+    __amdgpu_buffer_rsrc_t rc, rsc;
+    int tile0, tbytes, voff, sc_lane;
+    __device__ __forceinline__ void init(const WaveJob &J, int rows, int cols, int lane, int sc_lane_)
+    {
+        const int nb = is_cb<CLASS> ? J.bits : 4;  // bits per weight
+        const uint64_t cb = uniform((uint64_t)(uintptr_t)J.codes);
+        rc = __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)cb, 0,
+                                               (int)((long)rows * cols / 8 * nb), 0x00020000);
+        rsc = tensor_rsrc(J.scales);
+        tile0 = J.rb0 * J.G;
+        tbytes = 256 * nb;  // 16 x 128 weights
+        voff = lane * 4 * nb;  // 8, 12 or 16 bytes per lane
+        sc_lane = sc_lane_;
+    }
+    __device__ __forceinline__ void load(GroupBuf<CLASS, 1> &b, int g) const
+    {
+        const int tile = tile0 + g;
+        if constexpr (is_cb<CLASS>) {
+            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, voff, tile * tbytes, 0);
+            b.w[0][0] = v[0];
+            b.w[0][1] = v[1];
+            b.w[0][2] = v[2];
+            b.sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, tile * 32, 0);
+        } else {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, tile * 1024, 0);
+            b.w[0][0] = v[0];
+            b.w[0][1] = v[1];
+            b.w[0][2] = v[2];
+            b.w[0][3] = v[3];
+            b.sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rsc, sc_lane, tile * 128, 0);
+        }
+    }
+};
+
+// All G groups of the wave's tile: buffer d holds groups d, d + D, ... and
+// is refilled with the group D ahead once used (clamped to the last group,
+// so that every load is unconditional), except in the last round. The
+// buffers arrive holding groups 0 .. D-1 (clamped likewise). Clamped loads
+// that no group uses are waited for at the end: left pending they would be
+// waited for inside the next item's loop, where the wait takes every load in
+// flight with it. FMT: the code width (2, 3) or 4 (NVFP4), fixed per instance.
+template <int CLASS, int FMT>
+__device__ __forceinline__ void sm_stream(const SmTiles<CLASS> &T, int G, const _Float16 *Arow,
+                                          const uint32_t (&tab)[4],
+                                          GroupBuf<CLASS, 1> (&buf)[kSmDepth], floatx4 &acc)
+{
+    int g0 = 0;
+    for (; g0 + kSmDepth < G; g0 += kSmDepth) {
+#pragma unroll
+        for (int d = 0; d < kSmDepth; ++d) {
+            sm_group<CLASS, FMT>(buf[d], Arow + (g0 + d) * 128, tab, acc);
+            T.load(buf[d], min(g0 + d + kSmDepth, G - 1));
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < kSmDepth; ++d)
+        if (g0 + d < G)
+            sm_group<CLASS, FMT>(buf[d], Arow + (g0 + d) * 128, tab, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
+
+template <int CLASS>
+__global__ __launch_bounds__(kExpertThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void small_kernel(Params p)
+{
+    static_assert(!has6<CLASS>, "6-bit codes run on the persistent kernel");
+    extern __shared__ __align__(16) _Float16 Abuf[];  // staged rows (R x (cols + pad) halves), then the row-group table
+    __shared__ float s_u[2][16][16];    // up results of a gate/up item: [tile][row][token]
+    __shared__ int s_flag;
+    const Plan *P = p.plan;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int m = uniform(P->m), ngr = uniform(P->n_groups);
+    int *s_tab = (int *)((char *)Abuf + p.lds_tab);
+    const GroupLds s_grp{s_tab, s_tab + p.gcap, s_tab + 2 * p.gcap};
+    for (int i = tid; i < p.gcap; i += kExpertThreads) {
+        s_tab[i] = P->g_expert[i];
+        s_tab[p.gcap + i] = P->g_off[i];
+        s_tab[2 * p.gcap + i] = P->g_rows[i];
+    }
+    __syncthreads();
+    const int nsl = p.I / kSmGuRows, ndn = p.H / kSmDnRows;
+    const int n_gu = ngr * nsl, n_all = n_gu + ngr * ndn;
+    const int sc_lane = is_cb<CLASS> ? r16 * 2 : r16 * 8 + 2 * q;
+    float *const h_pre = p.gu_part;  // [bucket row][I]: SiLU(g) u, before the rotation
+    uint32_t done = 0;
+    for (int t = blockIdx.x; t < n_all; t += gridDim.x) {
+        Item it{};
+        it.valid = 1;
+        it.half = -1;
+        it.span = 1;
+        it.down = t >= n_gu;
+        const int tt = it.down ? t - n_gu : t;
+        const int per = it.down ? ndn : nsl;
+        it.u = tt / per;
+        const int sl = tt - it.u * per;  // row slice of the item
+        it.e = uniform(s_grp.expert[it.u]);
+        it.off = uniform(s_grp.off[it.u]);
+        it.R = uniform(s_grp.rows[it.u]);
+        const int tok = load_token(p, it, m, r16);
+        const DevTensor d = p.tensors[it.e * 3 + (it.down ? 2 : wave >> 1)];
+        WaveJob J;
+        J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
+        J.scales = (gu8p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.scales);
+        J.lut = (const uint16_t *)(uintptr_t)uniform((uint64_t)(uintptr_t)d.lut);
+        J.ts = __uint_as_float((uint32_t)uniform((int)__float_as_uint(d.tensor_scale)));
+        J.bits = uniform(d.bits);
+        J.G = it.down ? p.I / 128 : p.H / 128;
+        J.rb0 = it.down ? sl * (kSmDnRows / 16) + wave : sl * (kSmGuRows / 16) + (wave & 1);
+        J.g0 = 0;
+        const int cols = it.down ? p.I : p.H;
+        const int astr = cols + kLdsPadHalves;  // LDS row stride (halves)
+        SmTiles<CLASS> T;
+        T.init(J, it.down ? p.H : p.I, cols, lane, sc_lane);
+
+        GroupBuf<CLASS, 1> buf[kSmDepth];
+        u32x4 lut = u32x4{0, 0, 0, 0};
+        bool ok = true;
+        if (!it.down) {
+            // the activation rows first (their commit then waits for them
+            // only), then the codebook and the first D weight groups
+            const int cpr = cols / 8, last = it.R * cpr - 1;
+            // the thread index, opaque to the compiler: the chunk offsets
+            // are recomputed per item instead of being hoisted to the kernel
+            // start and held (or spilled) across the item loop
+            int ti = tid;
+            asm volatile("" : "+v"(ti));
+            u32x4 v[kSmStageIters];
+#pragma unroll
+            for (int k = 0; k < kSmStageIters; ++k) {
+                const int i = min(ti + k * kExpertThreads, last);
+                const int r = i / cpr;
+                v[k] = *(const u32x4 GLOBAL *)(p.xr + (size_t)__shfl(tok, r) * p.H + (i - r * cpr) * 8);
+            }
+            if constexpr (is_cb<CLASS>)
+                lut = load_lut_raw(J);
+#pragma unroll
+            for (int k = 0; k < kSmDepth; ++k)
+                T.load(buf[k], min(k, J.G - 1));
+            // every chunk is written, the clamped ones again with the same
+            // value: a write skipped on some path would leave its load's wait
+            // pending into the loop below, where it would wait for every load
+#pragma unroll
+            for (int k = 0; k < kSmStageIters; ++k) {
+                const int i = min(ti + k * kExpertThreads, last);
+                const int r = i / cpr;
+                *(u32x4 *)(Abuf + r * astr + (i - r * cpr) * 8) = v[k];
+            }
+        } else {
+            // the weights first: they do not depend on h and load during the wait
+            if constexpr (is_cb<CLASS>)
+                lut = load_lut_raw(J);
+#pragma unroll
+            for (int k = 0; k < kSmDepth; ++k)
+                T.load(buf[k], min(k, J.G - 1));
+            if (tid == 0)
+                s_flag = wait_h(p, it.u, (uint32_t)nsl);
+            __syncthreads();
+            ok = s_flag != 0;
+            // h~ = (1/sqrt 128) H_128 (s_I h) per token and 128-column block
+            // (codebook; NVFP4 stages h as it is), task c = (row c / nb,
+            // block c % nb) by wave c % 4, kSmRotBatch tasks' loads at a time
+            const int nb = p.I / 128, ntask = it.R * nb;
+            for (int c0 = wave; c0 < ntask; c0 += kExpertWaves * kSmRotBatch) {
+                uint64_t hv[kSmRotBatch];
+#pragma unroll
+                for (int j = 0; j < kSmRotBatch; ++j) {
+                    const int c = min(c0 + kExpertWaves * j, ntask - 1), r = c / nb, b = c - r * nb;
+                    hv[j] = ld_coherent((const uint64_t *)(h_pre + (size_t)(it.off + r) * p.I + b * 128 + 2 * lane));
+                }
+#pragma unroll
+                for (int j = 0; j < kSmRotBatch; ++j) {
+                    // clamped tasks are done again (same values, same place),
+                    // so that every load is consumed on every path
+                    const int c = min(c0 + kExpertWaves * j, ntask - 1);
+                    const int r = c / nb, b = c - r * nb, n = b * 128 + 2 * lane;
+                    const floatx2 hh = __builtin_bit_cast(floatx2, hv[j]);
+                    float v0 = hh[0], v1 = hh[1];
+                    if (p.format == kFmtCodebook) {
+                        v0 *= (float)p.signs_i[n];
+                        v1 *= (float)p.signs_i[n + 1];
+                        wave_fwht128(v0, v1);
+                        v0 *= kInvSqrt128;
+                        v1 *= kInvSqrt128;
+                    }
+                    *(half2v *)(Abuf + r * astr + n) = half2v{(_Float16)v0, (_Float16)v1};
+                }
+            }
+        }
+        __syncthreads();
+        uint32_t tab[4] = {0, 0, 0, 0};
+        if constexpr (is_cb<CLASS>) {
+            lut_tables(lut, tab);
+            // computed once here, not recomputed from the codebook inside
+            // the loop (where its loads look pending to the wait placement)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                asm volatile("" : "+v"(tab[i]));
+        }
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        const _Float16 *Arow = Abuf + min(r16, it.R - 1) * astr + q * 32;
+        // the instance for the wave's code width (wave-uniform: the gate and
+        // up tensors of a block may differ); no barrier inside
+        if constexpr (!is_cb<CLASS>)
+            sm_stream<CLASS, 4>(T, J.G, Arow, tab, buf, acc);
+        else if (J.bits == 3)
+            sm_stream<CLASS, 3>(T, J.G, Arow, tab, buf, acc);
+        else
+            sm_stream<CLASS, 2>(T, J.G, Arow, tab, buf, acc);
+        if constexpr (!is_cb<CLASS>)
+            acc *= J.ts;
+        // result: lane holds rows (tokens) 4q + j of W row r16 of the tile
+        if (it.down) {
+            int pr[4];  // pair index of row 4q + j (see load_token)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                pr[j] = __shfl(tok, 4 * q + j);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (ok && 4 * q + j < it.R)
+                    p.y_part[(size_t)pr[j] * p.H + J.rb0 * 16 + r16] = acc[j];
+        } else {
+            // the up waves hand their results to the gate waves
+            if (wave >= 2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * q + j < it.R)
+                        s_u[wave & 1][r16][4 * q + j] = acc[j];
+            __syncthreads();
+            if (wave < 2) {
+                const int n = sl * kSmGuRows + wave * 16 + r16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * q + j < it.R) {
+                        const float g = acc[j], u = s_u[wave][r16][4 * q + j];
+                        st_coherent(&h_pre[(size_t)(it.off + 4 * q + j) * p.I + n],
+                                    g / (1.0f + expf(-g)) * u);
+                    }
+            }
+            wait_stores();
+            __syncthreads();
+            if (tid == 0)
+                atomic_add_agent(&p.h_ready[it.u * kCtrStride], 1u);
+        }
+        ++done;
+        __syncthreads();  // the staged rows and s_u are the next item's
+    }
+    if (tid == 0 && done)
+        atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], done);
+}
+
+// ---------------------------------------------------------------------------
 // Combine
 // ---------------------------------------------------------------------------
 
@@ -1294,13 +1613,14 @@ void expert_kernel(Params p)
 // the shared expert's row (weight 1) when there is one. Block
 // (rb, t) covers rows rb*256 .. +255 of token t; runs after the expert
 // kernel, so plain loads see its partial sums.
-// One round of loads: every slot's weight and partial sums of the first two
-// splits, the shared expert's row and the error word are issued before any
-// is used (further splits, where a layer has more than two, follow in a
-// second round); then the sums, in the order above. Every load is issued
-// whatever k and the split count (indices past them are clamped to the last
-// slot / split and their values not used), so that the compiler can keep
-// them all in flight. KMAX: 8 or 16 slots. The scalar arguments come first:
+// Loads in rounds of up to 8 slots: a round's weights and partial sums of
+// the first two splits (and, before the first round, the shared expert's row
+// and the error word) are issued before any is used (further splits, where a
+// layer has more than two, follow separately); then that round's sums, in
+// the order above. Every load of a round is issued whatever k and the split
+// count (indices past them are clamped to the last slot / split and their
+// values not used), so that the compiler can keep them all in flight. KMAX:
+// 8 or 16 slots (one or two rounds). The scalar arguments come first:
 // the kernel-argument preload puts them in scalar registers at launch, so
 // the loads need not wait for the parameter block (they are also in p).
 template <int KMAX>
@@ -1673,7 +1993,7 @@ template <int CLASS, bool DOWN>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_kernel(Params p)
 {
-    extern __shared__ _Float16 pf_lds[];  // [2][64][kPfAStride]; the gate/up epilogue reuses it
+    extern __shared__ __align__(16) _Float16 pf_lds[];  // [2][64][kPfAStride]; the gate/up epilogue reuses it
     const Plan *P = p.plan;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -1787,6 +2107,25 @@ hipError_t launch_combine(const Params &p, int m, hipStream_t s)
         combine_kernel<kMaxTopK><<<dim3(p.n_rb2, m), dim3(64), 0, s>>>(
             p.y_part, p.wts, p.ctr, p.k, p.ks2, p.pair_cap, p.H, p.has_shared, p);
     return hipGetLastError();
+}
+
+static void *small_kernel_for(int format)
+{
+    return format == kFmtCodebook ? (void *)small_kernel<kFmtCodebook>
+                                  : (void *)small_kernel<kFmtNvfp4>;
+}
+
+hipError_t launch_small(const Params &p, int grid, size_t lds_bytes, hipStream_t s)
+{
+    void *args[] = {const_cast<Params *>(&p)};
+    return hipLaunchKernel(small_kernel_for(p.format), dim3(grid), dim3(kExpertThreads), args,
+                           lds_bytes, s);
+}
+
+hipError_t small_occupancy(int format, int *blocks_per_cu, size_t lds_bytes)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, small_kernel_for(format),
+                                                        kExpertThreads, lds_bytes);
 }
 
 hipError_t launch_expert(const Params &p, int grid, size_t lds_bytes, hipStream_t s)

@@ -115,5 +115,13 @@ hipError_t launch_prefill(const Params &p, int grid_groups, hipStream_t s);
 constexpr int kPrefillRows = 64;  // rows per prefill row group
 // Occupancy of the expert kernel for a given dynamic LDS size.
 hipError_t expert_occupancy(int format, int ng, bool six, int *blocks_per_cu, size_t lds_bytes);
+// Small-m kernel (runs of up to kSmallMaxTokens tokens when no tensor has
+// 6-bit codes): gate/up items of 32 rows and down items of 64 rows over all
+// columns, persistent grid; it stages R x max(H, I) fp16 activation rows with
+// at most kSmallStageElems elements.
+hipError_t launch_small(const Params &p, int grid, size_t lds_bytes, hipStream_t s);
+hipError_t small_occupancy(int format, int *blocks_per_cu, size_t lds_bytes);
+constexpr int kSmallMaxTokens = 4;
+constexpr int kSmallStageElems = 8 * 256 * 8;  // staging loads per thread x threads x 8 halves
 
 }  // namespace moe

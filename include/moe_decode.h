@@ -172,7 +172,13 @@ moe_status moe_decode_create(const moe_decode_config *cfg, moe_decode_t *out);
  * step runs grouped-GEMM prefill kernels instead of the persistent decode
  * kernel (page "LNA-CANON.md", section "起動": prefill batches of up to 512
  * tokens); a token's output then differs from a run at smaller m in rounding
- * only. Errors: MOE_E_INVALID, MOE_E_STREAM, MOE_E_HIP (launch failure).
+ * only. With very few tokens (at most 4, and only where every work item of
+ * the run fits in one round of a persistent grid: one token at top-8 on the
+ * 4096 x 2048 layer) a small-m kernel replaces the persistent one: its
+ * gate/up items cover 32 rows over all columns, so no split sums cross
+ * blocks; it is persistent too (the residency note above applies), and a
+ * token's output differs from the other kernels' in rounding only.
+ * Errors: MOE_E_INVALID, MOE_E_STREAM, MOE_E_HIP (launch failure).
  * Device faults surface at the caller's next sync.
  */
 moe_status moe_decode_run(moe_decode_t h, const void *x_bf16, const float *logits, float *out,

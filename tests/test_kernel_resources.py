@@ -53,3 +53,18 @@ def test_four_waves_per_simd_fit(kernel_meta, kind):
     assert found, kind
     for name, m in found:
         assert m["vgpr"] + m["agpr"] <= 128, (name, m)
+
+
+def test_dynamic_lds_arrays_are_16_byte_aligned():
+    """The dynamic LDS array starts right after the kernel's static LDS,
+    rounded up to the array's declared alignment. MFMA operands are read
+    and staged with 16-byte LDS accesses, which need 16-byte aligned
+    addresses: with the element type's 2-byte alignment the array started
+    12 bytes in and every such access was split."""
+    src = open(os.path.join(CSRC, "kernels.hip")).read()
+    decls = re.findall(r"extern __shared__[^;]*;", src)
+    assert decls
+    for d in decls:
+        if "uint32_t" in d:  # 4-byte accesses only (route bucketing)
+            continue
+        assert "__align__(16)" in d, d
