@@ -529,14 +529,17 @@ def test_nvfp4_every_finite_scale_code(w, m):
     parity(case)
 
 
-def test_gave_up_wait_surfaces_as_device_error(monkeypatch):
+@pytest.mark.parametrize("m", [8, 1])
+def test_gave_up_wait_surfaces_as_device_error(monkeypatch, m):
     # A bound of zero polls makes the down items' wait for h give up at
     # once (every kernel still ends normally): the run's output must be NaN,
     # the stats query and destroy must return MOE_E_DEVICE, and a handle
     # with the normal bound must run the same inputs correctly afterwards.
+    # m = 8 runs the persistent expert kernel, m = 1 the small-m kernel (its
+    # 8 row groups x (512/32 + 1024/64) items fit one round of its grid).
     import bit_quantized_moe_block_amd as B
     w = small_workload("spin", 64, 8, 1024, 512, bits_mix="alternate", config_id=520)
-    case = gen.make_case(w, 8)
+    case = gen.make_case(w, m)
     monkeypatch.setenv("MOE_DECODE_SPIN_LIMIT", "0")
     layer = DeviceLayer.from_case(case, max_tokens=8)
     monkeypatch.delenv("MOE_DECODE_SPIN_LIMIT")
@@ -548,6 +551,8 @@ def test_gave_up_wait_surfaces_as_device_error(monkeypatch):
         st = B.moe_decode_stats()
         B.lib().moe_decode_query(layer.handle, B.MOE_Q_STATS, C.byref(st), C.sizeof(st))
         assert st.error_word == 1
+        if m == 1:  # the small-m kernel's item count: 32-row gate/up, 64-row down items
+            assert st.items == st.hit_experts * (w.inter // 32 + w.hidden // 64)
         assert np.all(np.isnan(out))
     finally:
         with pytest.raises(B.MoeDecodeError) as ei:
