@@ -326,6 +326,11 @@ __device__ void bucket_block(const Params &p, int m, const int *s_ids)
         p.rows[q] = i;
         p.pos[i] = q;
     }
+    // the shared expert's rows m*k + t hold their own index: every bucket
+    // row's entry is then the pair index its down partial sums go under
+    if (p.has_shared)
+        for (int t = tid; t < m; t += kRouteThreads)
+            p.rows[np + t] = np + t;
     if (tid == 0) {
         p.offsets[E] = total;
         // gate/up items of span1 row blocks for the routed groups that fit in
@@ -556,6 +561,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void GLOBAL 
 {
     const uint64_t b = uniform((uint64_t)(uintptr_t)base);
     return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)b, 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base)
+{
+    return tensor_rsrc((const void GLOBAL *)(uintptr_t)base);
 }
 
 // Load group j (absolute group g0 + j) of job J into b (NT tiles). KB: codebook bits
@@ -871,18 +880,22 @@ __device__ __forceinline__ DescRaw load_desc(const Params &p, const Item &it, in
     return d;
 }
 
-// For lane r16, bucket row q = off + min(r16, R-1) of the item's group: a
-// gate/up item's token of q, a down item's pair index of q (t*k + j for a
-// routed row, q itself for the shared expert's row m*k + t), under which its
-// partial sums are stored. Loaded one item ahead, with the item's descriptor.
-__device__ __forceinline__ int load_token(const Params &p, const Item &it, int m, int r16)
+// For lane r16, bucket row q = off + min(r16, R-1) of the item's group: the
+// pair index of q (t*k + j for a routed row, q itself for the shared expert's
+// row m*k + t: the bucket row list holds both), under which a down item's
+// partial sums are stored. Loaded one item ahead with the item's descriptor,
+// unconditionally (an invalid item reads entry 0), and nothing is computed
+// from it at the load: the wait for it lands where it is first used.
+__device__ __forceinline__ int load_pair(const Params &p, const Item &it, int r16)
 {
-    if (!it.valid)
-        return 0;
-    const int q = it.off + min(r16, it.R - 1);
-    if (it.down)
-        return q < m * p.k ? p.rows[q] : q;
-    return q < m * p.k ? p.rows[q] / p.k : q - m * p.k;
+    const int q = it.valid ? it.off + min(r16, it.R - 1) : 0;
+    return p.rows[q];
+}
+
+// The token of pair index pr (m*k = mk routed pairs, then the shared rows).
+__device__ __forceinline__ int pair_token(int pr, int mk, int k)
+{
+    return pr < mk ? pr / k : pr - mk;
 }
 
 // The matrix part wave `wave` computes for item `it`: a gate/up item's 128
@@ -975,6 +988,11 @@ __device__ void finish_h(const Params &p, int off, int R, int rb)
                         __builtin_bit_cast(uint32_t, half2v{(_Float16)v0, (_Float16)v1}));
         }
     }
+    // every load above complete on every path (the caller waits for the
+    // stores next anyway): a load taken on one path only would otherwise
+    // look pending in the next item, whose first register writes would then
+    // wait for every load in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 // Wait until row group u's h counter reaches `target` (bounded): every
@@ -1015,33 +1033,54 @@ struct Stage {
     static constexpr int ASTRIDE = KC + kLdsPadHalves;   // LDS row stride (halves)
     u32x4 v[ITERS];
 
+    // tok: the token of row r16 (lane r of each wave holds row r's). The two
+    // kinds of item take separate loops on a scalar branch: code shared by
+    // both paths would make a load of one path look pending in the other,
+    // where the compiler then waits for it before every staging load.
+    // Offsets are 32-bit (the buffers are far below 2 GB).
     __device__ __forceinline__ void issue(const Params &p, const Item &it, int tok)
     {
         const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
         const int wave_first = uniform(tid & ~63);
         const int col0 = it.kq * KC;
 #pragma unroll
-        for (int k = 0; k < ITERS; ++k) {
+        for (int k = 0; k < ITERS; ++k)
             v[k] = u32x4{0, 0, 0, 0};
-            if (wave_first + k * kExpertThreads > last)
-                continue;
-            const int i = min(tid + k * kExpertThreads, last);
-            const int r = i / CHUNKS, cc = (i - r * CHUNKS) * 8;
-            if (it.down) {
-                // h~ rows off..off+R-1 are consecutive: one coherent buffer
-                const _Float16 *base = p.hr + (size_t)it.off * p.I + col0;
-                v[k] = ld_coherent16(base, (uint32_t)((r * p.I + cc) * 2));
-            } else {
-                // token of row r: lane r of the wave holds it (see load_token)
-                const _Float16 *row = p.xr + (size_t)__shfl(tok, r) * p.H + col0;
-                v[k] = *(const u32x4 GLOBAL *)(row + cc);
+        if (uniform(it.down)) {
+            // h~ rows off..off+R-1 are consecutive: one coherent buffer
+            const _Float16 *base = p.hr + (size_t)uniform(it.off) * p.I + col0;
+#pragma unroll
+            for (int k = 0; k < ITERS; ++k) {
+                if (wave_first + k * kExpertThreads > last)
+                    continue;
+                const int i = min(tid + k * kExpertThreads, last);
+                const int r = i / CHUNKS, cc = (i - r * CHUNKS) * 8;
+                v[k] = ld_coherent16(base, (uint32_t)(r * p.I + cc) * 2u);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = buf_rsrc(p.xr + col0);
+            const uint32_t hb = (uint32_t)p.H * 2u;  // bytes per activation row
+#pragma unroll
+            for (int k = 0; k < ITERS; ++k) {
+                if (wave_first + k * kExpertThreads > last)
+                    continue;
+                const int i = min(tid + k * kExpertThreads, last);
+                const int r = i / CHUNKS, cc = (i - r * CHUNKS) * 8;
+                const uint32_t off = __umul24((uint32_t)__shfl(tok, r), hb) + (uint32_t)cc * 2u;
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
             }
         }
     }
+    // Every staging load is complete after the first wait below on every
+    // path (they are the item's last loads, so nothing else is waited for):
+    // waited for only inside the rounds a wave writes, the loads of the
+    // rounds it skips would look pending past the item, and the next item's
+    // first writes of these registers would wait for every load in flight.
     __device__ __forceinline__ void commit(const Item &it, _Float16 *A) const
     {
         const int tid = threadIdx.x, last = it.R * CHUNKS - 1;
         const int wave_first = uniform(tid & ~63);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
         for (int k = 0; k < ITERS; ++k) {
             if (wave_first + k * kExpertThreads > last)
@@ -1054,41 +1093,54 @@ struct Stage {
 };
 
 // Store the partial sums of one row block of an item (rows rb0.. of job J).
-// Gate/up partials go out agent-coherent for the finishing block; down
-// partials are read only by the combine kernel, after this kernel ends.
-// Results of an item: gate/up partials under the bucket row, down partials
-// under the row's pair index (tok: see load_token), so that the combine reads
-// them without the bucket positions.
+// Gate/up partials go out agent-coherent (sc1) for the finishing block, under
+// the bucket row; down partials, read only by the combine kernel after this
+// kernel ends, under the row's pair index (pair: see load_pair), so that the
+// combine reads them without the bucket positions. One 32-bit offset per
+// token row; the tiles differ by a constant 64 bytes.
 template <int CLASS>
 __device__ __forceinline__ void store_rows(const Params &p, const Item &it, const WaveJob &J,
-                                           const floatx4 (&acc)[kWaveRB], int tok)
+                                           const floatx4 (&acc)[kWaveRB], int pair)
 {
     const int tid = threadIdx.x;
-    // the lane index, opaque to the compiler: the addresses below are
+    // the lane index, opaque to the compiler: the offsets below are
     // recomputed at each call instead of being hoisted to the kernel start
     // and held (or spilled) across the whole item loop
     int lane = tid & 63;
     asm volatile("" : "+v"(lane));
-    const int proj = item_proj(it, tid >> 6);
     const int ntiles = has6<CLASS> && J.bits == 6 ? kWaveRB / 2 : kWaveRB;  // 6-bit: 2 per wave
-    int pr[4];  // down: pair index of row 4 (lane / 16) + j, from the lane holding it
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        pr[j] = __shfl(tok, 4 * (lane >> 4) + j);
-#pragma unroll
-    for (int i = 0; i < kWaveRB; ++i)
+    const int q4 = 4 * (lane >> 4), R = uniform(it.R);
+    const uint32_t col = (uint32_t)(J.rb0 * 16 + (lane & 15)) * 4u;  // byte offset of W row n
+    if (uniform(it.down)) {
+        const __amdgpu_buffer_rsrc_t rs =
+            buf_rsrc(p.y_part + (size_t)uniform(it.kq) * p.pair_cap * p.H);
+        const uint32_t hb = (uint32_t)p.H * 4u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = 4 * (lane >> 4) + j;
-            if (i < ntiles && r < it.R) {
-                const size_t row = (size_t)it.kq * p.pair_cap + (it.down ? pr[j] : it.off + r);
-                const int n = (J.rb0 + i) * 16 + (lane & 15);
-                if (it.down)
-                    p.y_part[row * p.H + n] = acc[i][j];
-                else
-                    st_coherent(&p.gu_part[(row * 2 + proj) * p.I + n], acc[i][j]);
-            }
+            const uint32_t off = __umul24((uint32_t)__shfl(pair, q4 + j), hb) + col;
+            if (q4 + j < R)
+#pragma unroll
+                for (int i = 0; i < kWaveRB; ++i)
+                    if (i < ntiles)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j]), rs,
+                                                              (int)off, i * 64, 0);
         }
+    } else {
+        const int proj = item_proj(it, tid >> 6);
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(
+            p.gu_part + (((size_t)uniform(it.kq) * p.pair_cap + uniform(it.off)) * 2 + proj) * p.I);
+        const uint32_t rb = (uint32_t)p.I * 8u;  // bytes per bucket row (gate and up)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t off = __umul24((uint32_t)(q4 + j), rb) + col;
+            if (q4 + j < R)
+#pragma unroll
+                for (int i = 0; i < kWaveRB; ++i)
+                    if (i < ntiles)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j]), rs,
+                                                              (int)off, i * 64, 16 /* sc1 */);
+        }
+    }
 }
 
 // After a gate/up item's stores: once they are acknowledged, count the item's
@@ -1183,7 +1235,7 @@ void expert_kernel(Params p)
     // share a CU, dispatched in that order
     const int rot = uniform((int)(blockIdx.x / max(1u, gridDim.x / 4u))) % 3;
     Item cur = make_item(p, n_items, n_items1, n_sg, n_wide, s_grp, ticket);
-    int tok = load_token(p, cur, m, r16);
+    int pair = load_pair(p, cur, r16);
     uint32_t done = 0;
     if (cur.valid) {
         GroupBuf<CLASS> bA, bB;
@@ -1202,7 +1254,7 @@ void expert_kernel(Params p)
             const Item nxt = make_item(p, n_items, n_items1, n_sg, n_wide, s_grp,
                                        last ? nxt_ticket : n_items);
             const DescRaw dn = load_desc(p, nxt, wave);
-            const int tok_n = load_token(p, nxt, m, r16);
+            const int pair_n = load_pair(p, nxt, r16);
 
             bool ok = true;
             if (sb == 0) {
@@ -1230,7 +1282,7 @@ void expert_kernel(Params p)
                     ok = sm.flag != 0;
                 }
                 St st;
-                st.issue(p, cur, tok);
+                st.issue(p, cur, pair_token(pair, m * p.k, p.k));
                 st.commit(cur, Abuf);
                 // a 6-bit codebook goes to the wave pair's LDS slot (the waves
                 // sharing it write the same values)
@@ -1264,7 +1316,7 @@ void expert_kernel(Params p)
                 for (int i = 0; i < kWaveRB; ++i)
                     acc[i] *= J.ts;
             if (ok)
-                store_rows<CLASS>(p, cur, J, acc, tok);
+                store_rows<CLASS>(p, cur, J, acc, pair);
             if (!last) {
                 ++sb;
                 J = JN;
@@ -1278,8 +1330,12 @@ void expert_kernel(Params p)
                 break;
             ticket = nxt_ticket;
             cur = nxt;
-            tok = tok_n;
+            pair = pair_n;
             sb = 0;
+            // every descriptor word stays live until here: one the kernel
+            // does not use would free its register for a temporary, whose
+            // first write then waits for the load still on its way into it
+            asm volatile("" ::"v"(dn.d0), "v"(dn.d1));
             J = make_job<CLASS, NG>(p, dn, nxt, wave);
         }
     }
@@ -1452,7 +1508,7 @@ void small_kernel(Params p)
         it.e = uniform(s_grp.expert[it.u]);
         it.off = uniform(s_grp.off[it.u]);
         it.R = uniform(s_grp.rows[it.u]);
-        const int tok = load_token(p, it, m, r16);
+        const int pair = load_pair(p, it, r16);
         const DevTensor d = p.tensors[it.e * 3 + (it.down ? 2 : wave >> 1)];
         WaveJob J;
         J.codes = (gu32p)(uintptr_t)uniform((uint64_t)(uintptr_t)d.codes);
@@ -1480,12 +1536,16 @@ void small_kernel(Params p)
             // start and held (or spilled) across the item loop
             int ti = tid;
             asm volatile("" : "+v"(ti));
+            const int tok = pair_token(pair, m * p.k, p.k);
+            const __amdgpu_buffer_rsrc_t rx = buf_rsrc(p.xr);
             u32x4 v[kSmStageIters];
 #pragma unroll
             for (int k = 0; k < kSmStageIters; ++k) {
                 const int i = min(ti + k * kExpertThreads, last);
                 const int r = i / cpr;
-                v[k] = *(const u32x4 GLOBAL *)(p.xr + (size_t)__shfl(tok, r) * p.H + (i - r * cpr) * 8);
+                const uint32_t off = __umul24((uint32_t)__shfl(tok, r), (uint32_t)p.H * 2u) +
+                                     (uint32_t)(i - r * cpr) * 16u;
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
             }
             if constexpr (is_cb<CLASS>)
                 lut = load_lut_raw(J);
@@ -1566,14 +1626,15 @@ void small_kernel(Params p)
             acc *= J.ts;
         // result: lane holds rows (tokens) 4q + j of W row r16 of the tile
         if (it.down) {
-            int pr[4];  // pair index of row 4q + j (see load_token)
+            const __amdgpu_buffer_rsrc_t ry = buf_rsrc(p.y_part);
+            const uint32_t col = (uint32_t)(J.rb0 * 16 + r16) * 4u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                pr[j] = __shfl(tok, 4 * q + j);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                // pair index of row 4q + j (see load_pair)
+                const uint32_t off = __umul24((uint32_t)__shfl(pair, 4 * q + j), (uint32_t)p.H * 4u) + col;
                 if (ok && 4 * q + j < it.R)
-                    p.y_part[(size_t)pr[j] * p.H + J.rb0 * 16 + r16] = acc[j];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j]), ry, (int)off, 0, 0);
+            }
         } else {
             // the up waves hand their results to the gate waves
             if (wave >= 2)
