@@ -104,6 +104,18 @@ __device__ __forceinline__ void wait_stores()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Block barrier that orders LDS only: the wave's LDS accesses complete, then
+// s_barrier; global loads and stores in flight stay in flight (the fences of
+// __syncthreads wait for every one of them). The signal fences keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // In-wave 128-point Walsh-Hadamard transform (Sylvester order) of the pair
@@ -939,6 +951,9 @@ __device__ void finish_h(const Params &p, int off, int R, int rb)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = rb * 128 + 2 * lane;
+    // the signs of the lane's two columns (codebook), loaded once with the
+    // first sums
+    const uint16_t sg = p.format == kFmtCodebook ? *(const uint16_t *)(p.signs_i + n) : 0;
     constexpr int TPP = 2;  // tokens per pass
     for (int t0 = wave; t0 < R; t0 += TPP * kExpertWaves) {
         floatx2 g[TPP], u[TPP];
@@ -978,8 +993,8 @@ __device__ void finish_h(const Params &p, int off, int R, int rb)
             float v0 = g[ti][0] / (1.0f + expf(-g[ti][0])) * u[ti][0];
             float v1 = g[ti][1] / (1.0f + expf(-g[ti][1])) * u[ti][1];
             if (p.format == kFmtCodebook) {
-                v0 *= (float)p.signs_i[n];
-                v1 *= (float)p.signs_i[n + 1];
+                v0 *= (float)(int8_t)(sg & 0xFF);
+                v1 *= (float)(int8_t)(sg >> 8);
                 wave_fwht128(v0, v1);
                 v0 *= kInvSqrt128;
                 v1 *= kInvSqrt128;
@@ -1278,7 +1293,7 @@ void expert_kernel(Params p)
                     __builtin_amdgcn_s_setprio(0);  // waiting yields to the others
                     if (tid == 0)
                         sm.flag = wait_h(p, cur.u, (uint32_t)p.n_rb1);
-                    __syncthreads();
+                    lds_barrier();  // the weight groups stay in flight
                     ok = sm.flag != 0;
                 }
                 St st;
@@ -1325,7 +1340,10 @@ void expert_kernel(Params p)
             if (ok)
                 complete_item(p, cur, sm);
             ++done;
-            __syncthreads();
+            // the staged rows and sm are the next item's (a down item's
+            // partial-sum stores need no acknowledgement: read by the
+            // combine kernel only)
+            lds_barrier();
             if (!nxt.valid)
                 break;
             ticket = nxt_ticket;
@@ -1570,7 +1588,7 @@ void small_kernel(Params p)
                 T.load(buf[k], min(k, J.G - 1));
             if (tid == 0)
                 s_flag = wait_h(p, it.u, (uint32_t)nsl);
-            __syncthreads();
+            lds_barrier();  // the weight groups stay in flight
             ok = s_flag != 0;
             // h~ = (1/sqrt 128) H_128 (s_I h) per token and 128-column block
             // (codebook; NVFP4 stages h as it is), task c = (row c / nb,
@@ -1578,10 +1596,14 @@ void small_kernel(Params p)
             const int nb = p.I / 128, ntask = it.R * nb;
             for (int c0 = wave; c0 < ntask; c0 += kExpertWaves * kSmRotBatch) {
                 uint64_t hv[kSmRotBatch];
+                uint16_t sg[kSmRotBatch];  // the signs of the lane's two columns
 #pragma unroll
                 for (int j = 0; j < kSmRotBatch; ++j) {
                     const int c = min(c0 + kExpertWaves * j, ntask - 1), r = c / nb, b = c - r * nb;
                     hv[j] = ld_coherent((const uint64_t *)(h_pre + (size_t)(it.off + r) * p.I + b * 128 + 2 * lane));
+                    sg[j] = 0;
+                    if constexpr (is_cb<CLASS>)
+                        sg[j] = *(const uint16_t *)(p.signs_i + b * 128 + 2 * lane);
                 }
 #pragma unroll
                 for (int j = 0; j < kSmRotBatch; ++j) {
@@ -1591,9 +1613,9 @@ void small_kernel(Params p)
                     const int r = c / nb, b = c - r * nb, n = b * 128 + 2 * lane;
                     const floatx2 hh = __builtin_bit_cast(floatx2, hv[j]);
                     float v0 = hh[0], v1 = hh[1];
-                    if (p.format == kFmtCodebook) {
-                        v0 *= (float)p.signs_i[n];
-                        v1 *= (float)p.signs_i[n + 1];
+                    if constexpr (is_cb<CLASS>) {
+                        v0 *= (float)(int8_t)(sg[j] & 0xFF);
+                        v1 *= (float)(int8_t)(sg[j] >> 8);
                         wave_fwht128(v0, v1);
                         v0 *= kInvSqrt128;
                         v1 *= kInvSqrt128;
@@ -1602,7 +1624,7 @@ void small_kernel(Params p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();  // staged rows written; the weight groups stay in flight
         uint32_t tab[4] = {0, 0, 0, 0};
         if constexpr (is_cb<CLASS>) {
             lut_tables(lut, tab);
@@ -1642,7 +1664,7 @@ void small_kernel(Params p)
                 for (int j = 0; j < 4; ++j)
                     if (4 * q + j < it.R)
                         s_u[wave & 1][r16][4 * q + j] = acc[j];
-            __syncthreads();
+            lds_barrier();
             if (wave < 2) {
                 const int n = sl * kSmGuRows + wave * 16 + r16;
 #pragma unroll
@@ -1659,7 +1681,7 @@ void small_kernel(Params p)
                 atomic_add_agent(&p.h_ready[it.u * kCtrStride], 1u);
         }
         ++done;
-        __syncthreads();  // the staged rows and s_u are the next item's
+        lds_barrier();  // the staged rows and s_u are the next item's
     }
     if (tid == 0 && done)
         atomic_add_agent(&p.ctr->items_done[blockIdx.x % kDoneSlots], done);
@@ -2016,11 +2038,13 @@ __device__ __forceinline__ void pf_run(const Params &p, _Float16 *pf_lds, const 
                     }
         __syncthreads();
         const int n = rb * 128 + 2 * lane;
+        // the lane's two signs (codebook), once rather than per row
+        const uint16_t sg = p.format == kFmtCodebook ? *(const uint16_t *)(p.signs_i + n) : 0;
         for (int row = wave; row < R; row += kPfWaves) {
             float v0 = hb[row * kPfHStride + 2 * lane], v1 = hb[row * kPfHStride + 2 * lane + 1];
             if (p.format == kFmtCodebook) {
-                v0 *= (float)p.signs_i[n];
-                v1 *= (float)p.signs_i[n + 1];
+                v0 *= (float)(int8_t)(sg & 0xFF);
+                v1 *= (float)(int8_t)(sg >> 8);
                 wave_fwht128(v0, v1);
                 v0 *= kInvSqrt128;
                 v1 *= kInvSqrt128;
