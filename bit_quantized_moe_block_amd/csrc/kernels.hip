@@ -1072,6 +1072,10 @@ struct Stage {
                 const int r = i / CHUNKS, cc = (i - r * CHUNKS) * 8;
                 v[k] = ld_coherent16(base, (uint32_t)(r * p.I + cc) * 2u);
             }
+            // complete here, in their own branch (commit needs them next
+            // anyway): the compiler's wait placement otherwise takes them
+            // for pending at the start of the gate/up branch
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         } else {
             const __amdgpu_buffer_rsrc_t rs = buf_rsrc(p.xr + col0);
             const uint32_t hb = (uint32_t)p.H * 2u;  // bytes per activation row
