@@ -20,9 +20,12 @@ scaled by the counters' reading of a plain copy of known size
 those counters were taken. `cpu_baseline` times the CPU oracle on a bounded
 sample of the same workload (one whole layer: median of 5 runs on every core of
 the process, plus a one-thread run on two tokens). The default run also sweeps
-m = 1, 2, 4, 8, 16, 24 on the same 43 resident layers (`m_sweep`), and reports two
-probes (include/moe_probe.h): a plain streaming read of 4 GiB and the graph-replay
-floor of three empty kernels per layer (`probes`), with the run's provenance.
+m = 1, 2, 4, 8, 16, 24 on the same 43 resident layers (`m_sweep`), and reports the
+probes of include/moe_probe.h (`probes`): a plain streaming read of 4 GiB, the
+graph-replay floor of three empty kernels per layer, the issue rates of the decode
+step's decode and MFMA halves on register operands (cycles per MFMA step per SIMD,
+four waves per SIMD), and a 1 GiB streaming read whose units are claimed from one
+or eight shared counters against a static order, with the run's provenance.
 """
 import argparse
 import hashlib
@@ -162,6 +165,12 @@ def probe_lib():
         L.moe_probe_lds_read128.restype = C.c_int
         L.moe_probe_lds_read128.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                             C.c_void_p]
+        L.moe_probe_compute_rate.restype = C.c_int
+        L.moe_probe_compute_rate.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                             C.c_void_p, C.c_void_p]
+        L.moe_probe_ticket_read.restype = C.c_int
+        L.moe_probe_ticket_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32,
+                                            C.c_void_p, C.c_void_p, C.c_void_p]
         _probe = L
     return _probe
 
@@ -218,6 +227,82 @@ def probe_lds_layouts(dev, blocks=1024, iters=256):
             e1.synchronize()
         us = e0.elapsed_time(e1) * 1e3
         out.append((layout, us, us * 1e-6 * 2.4e9 / reads_per_cu))
+    return out
+
+
+COMPUTE_MODES = ("decode only (+4 VALU xor fold per step)", "MFMA only (+ group-scale FMAs)",
+                 "decode into MFMA (the decode kernels' inner step)",
+                 "decode into 4 v_dot2_f32_f16 (one token, no MFMA)")
+
+
+def probe_compute_rates(dev, iters=2048):
+    """Issue rates of the decode step's halves on register operands (3-bit
+    codebook tile, 4 MFMA steps per round): one launch per mode after a
+    warm-up, 4 blocks of 4 waves per CU (4 waves per SIMD, as the decode
+    kernels run). Returns the shader clock (GHz, from block 0's s_memtime
+    against s_memrealtime) and per mode the nanoseconds and shader cycles per
+    MFMA step per SIMD."""
+    import torch
+    L = probe_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 4 * cus
+    simds = 4 * cus
+    steps_per_simd = blocks * 4 * iters * 4 / simds
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for mode in range(len(COMPUTE_MODES)):
+        for timed in (False, True):
+            e0.record(s)
+            rc = L.moe_probe_compute_rate(mode, blocks, iters, clk.data_ptr(), sink.data_ptr(),
+                                          s.cuda_stream)
+            e1.record(s)
+            if rc:
+                raise RuntimeError(f"moe_probe_compute_rate: HIP error {-rc}")
+            e1.synchronize()
+        c = clk.cpu().tolist()
+        ghz = (c[2] - c[0]) / ((c[3] - c[1]) / 100e6) / 1e9 if c[3] > c[1] else float("nan")
+        ns = e0.elapsed_time(e1) * 1e6 / steps_per_simd
+        out.append({"mode": mode, "desc": COMPUTE_MODES[mode], "ns_per_step": round(ns, 3),
+                    "cycles_per_step": round(ns * ghz, 1), "clock_ghz": round(ghz, 3)})
+    return out
+
+
+TICKET_MODES = ("static order", "one shared counter", "eight counters")
+
+
+def probe_tickets(dev, mib=1024, reps=3):
+    """A streaming read of `mib` MiB in 64 KiB units, the units taken in a
+    static order or claimed from one or eight shared counters: best GB/s over
+    a few grid sizes per mode."""
+    import torch
+    L = probe_lib()
+    nbytes = mib << 20
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    ctr = torch.zeros(256, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for mode in range(len(TICKET_MODES)):
+        best, best_grid = 1e30, 0
+        for grid in (1024, 2048, 4096):
+            for _ in range(reps):
+                e0.record(s)
+                rc = L.moe_probe_ticket_read(buf.data_ptr(), nbytes, grid, mode, ctr.data_ptr(),
+                                             sink.data_ptr(), s.cuda_stream)
+                e1.record(s)
+                if rc:
+                    raise RuntimeError(f"moe_probe_ticket_read: HIP error {-rc}")
+                e1.synchronize()
+                t = e0.elapsed_time(e1)
+                if t < best:
+                    best, best_grid = t, grid
+        out.append({"mode": mode, "desc": TICKET_MODES[mode],
+                    "gbs": round(nbytes / (best * 1e-3) / 1e9, 1), "grid": best_grid})
+    del buf
     return out
 
 
@@ -432,12 +517,20 @@ def main():
     if not args.no_probes:
         gbs, grid = probe_plain_read(dev)
         floor = probe_launch_floor(dev, max(n_layers, 1))
+        rates = probe_compute_rates(dev)
+        tickets = probe_tickets(dev)
         probes = {"plain_read_gbs": round(gbs, 1), "plain_read_frac": round(gbs / HBM_PEAK_GBS, 4),
                   "plain_read_grid": grid,
                   "launch_floor_us_per_layer": round(floor, 2),
-                  "launch_floor_kernels": 3 * max(n_layers, 1)}
+                  "launch_floor_kernels": 3 * max(n_layers, 1),
+                  "compute_rates": rates, "ticket_read": tickets}
         log(f"probes: plain read {gbs:.0f} GB/s ({grid} blocks), launch floor "
             f"{floor:.2f} us per layer (3 empty kernels per layer in one graph)")
+        for r in rates:
+            log(f"probes: {r['desc']}: {r['cycles_per_step']} cycles per MFMA step per SIMD "
+                f"({r['ns_per_step']} ns, clock {r['clock_ghz']} GHz)")
+        for r in tickets:
+            log(f"probes: streaming read, {r['desc']}: {r['gbs']} GB/s ({r['grid']} blocks)")
 
     # ---- CPU oracle on a bounded sample (layer 0 of the workload, all m
     # tokens when m <= 24, else the first 16): median of 5 runs after one

@@ -1,10 +1,14 @@
 // Measurement probes (include/moe_probe.h): a plain streaming read of a
-// device buffer, an empty kernel and the LDS read pattern of the MFMA
-// activation operands. Nothing of the decode step is computed here.
+// device buffer, an empty kernel, the LDS read pattern of the MFMA
+// activation operands, the issue rates of the decode step's halves (the
+// decode kernels' own decode sequence, from decode_step.h, on register
+// operands: no weights, no layer) and a streaming read whose units are
+// claimed from shared counters.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/moe_probe.h"
+#include "decode_step.h"
 
 namespace {
 
@@ -77,7 +81,164 @@ __global__ __launch_bounds__(256) void lds_read128(int layout, int iters, uint32
         sink[0] = f;
 }
 
+// Issue rates of one 128-column group of a 3-bit tile (4 MFMA steps of 8
+// weights per lane), all operands in registers: the slot words change every
+// round by an xor with the round index (one VALU op per word and round, in
+// every mode). MODE 0: decode only, each step's four output words xor-folded;
+// 1: MFMA only (a fixed B operand) and the group-scale FMAs; 2: decode into
+// the MFMA and the group-scale FMAs (the decode kernels' inner step); 3:
+// decode into four v_dot2_f32_f16 products for one token (the products on
+// the VALU instead of the MFMA). Thread 0 of block 0 records the shader clock
+// (s_memtime) and the 100 MHz constant clock (s_memrealtime) before and after
+// its rounds in clk[0..3].
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void compute_rate(int iters, uint32_t seed, unsigned long long *clk, uint32_t *sink)
+{
+    using namespace moe;
+    const int lane = threadIdx.x & 63;
+    uint32_t tab[4];
+    // a codebook of eight fp16 entries of magnitude 0.25 .. 2
+    lut_tables(u32x4{0xB800BC00u ^ (seed & 1u), 0x38003400u, 0xB4003C00u, 0x40003000u}, tab);
+    const uint32_t w[3] = {seed * 0x9E3779B9u + (uint32_t)lane, (seed + (uint32_t)lane) * 0x85EBCA6Bu,
+                           (uint32_t)lane * 0xC2B2AE35u + seed};
+    half8 a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            a[s][e] = (_Float16)(0.001f * (float)((lane + 3 * s + e) & 31));
+    const half8 bconst = a[(lane >> 4) & 3];
+    const float f = 0.5f + (float)(seed & 1u);
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    float dacc = 0.f;
+    uint32_t fold = 0;
+    unsigned long long t0 = 0, r0 = 0;
+    const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+    if (timer) {
+        t0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    for (int it = 0; it < iters; ++it) {
+        const uint32_t x[3] = {w[0] ^ (uint32_t)it, w[1] ^ (uint32_t)it, w[2] ^ (uint32_t)it};
+        floatx4 cc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if constexpr (MODE == 0 || MODE == 2 || MODE == 3) {
+                const half8 bv = decode_step<3>(x, s, tab, half2v{1, 1});
+                if constexpr (MODE == 0) {
+                    const u32x4 u = __builtin_bit_cast(u32x4, bv);
+                    fold ^= u[0] ^ u[1] ^ u[2] ^ u[3];
+                } else if constexpr (MODE == 2) {
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], bv, cc, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dacc = __builtin_amdgcn_fdot2(
+                            half2v{a[s][2 * e], a[s][2 * e + 1]}, half2v{bv[2 * e], bv[2 * e + 1]},
+                            dacc, false);
+                }
+            } else {
+                cc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], bconst, cc, 0, 0, 0);
+            }
+        }
+        if constexpr (MODE == 1 || MODE == 2)
+            acc += f * cc;
+    }
+    if (timer) {
+        clk[0] = t0;
+        clk[1] = r0;
+        clk[2] = __builtin_amdgcn_s_memtime();
+        clk[3] = __builtin_amdgcn_s_memrealtime();
+    }
+    const uint32_t v = fold ^ __float_as_uint(dacc) ^ __float_as_uint(acc[0] + acc[1] + acc[2] + acc[3]);
+    if (v == 0x9E3779B9u)
+        sink[0] = v;
+}
+
+// Units of 64 KiB (4096 16-byte loads, 16 per thread, all in flight) read by
+// `gridDim.x` blocks of 256 threads, one unit at a time. MODE 0: block b
+// reads units b, b + G, ... (a static order); 1: each unit is claimed from
+// one counter (thread 0's agent-scope atomic add, handed to the block
+// through LDS); 2: from eight counters, 128 bytes apart (block b claims from
+// counter b % 8, whose k-th claim is unit b % 8 + 8 k).
+constexpr int kUnit16 = 4096;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ticket_read(const u32x4 *__restrict__ buf, uint32_t units,
+                                                   uint32_t *ctr, uint32_t *sink)
+{
+    __shared__ uint32_t s_claim;
+    const uint32_t nq = MODE == 2 ? 8u : 1u, q = blockIdx.x % nq;
+    u32x4 acc = u32x4{0, 0, 0, 0};
+    for (uint32_t k = 0;; ++k) {
+        uint32_t u;
+        if constexpr (MODE == 0) {
+            u = blockIdx.x + k * gridDim.x;
+        } else {
+            if (threadIdx.x == 0)
+                s_claim = __hip_atomic_fetch_add(&ctr[q * 32], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            u = q + nq * s_claim;
+            __syncthreads();
+        }
+        if (u >= units)
+            break;
+        const u32x4 *p = buf + (size_t)u * kUnit16 + threadIdx.x;
+        u32x4 v[kUnit16 / 256];
+#pragma unroll
+        for (int j = 0; j < kUnit16 / 256; ++j)
+            v[j] = p[j * 256];
+#pragma unroll
+        for (int j = 0; j < kUnit16 / 256; ++j)
+            acc ^= v[j];
+    }
+    const uint32_t f = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (f == 0x9E3779B9u)
+        sink[0] = f;
+}
+
 }  // namespace
+
+extern "C" int moe_probe_compute_rate(int32_t mode, int32_t blocks, int32_t iters,
+                                      unsigned long long *clk, uint32_t *sink, void *hip_stream)
+{
+    if (mode < 0 || mode > 3 || blocks < 1 || iters < 1 || !clk || !sink)
+        return -(int)hipErrorInvalidValue;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    const dim3 g(blocks), b(256);
+    const uint32_t seed = 0x2545F491u;
+    switch (mode) {
+    case 0: compute_rate<0><<<g, b, 0, s>>>(iters, seed, clk, sink); break;
+    case 1: compute_rate<1><<<g, b, 0, s>>>(iters, seed, clk, sink); break;
+    case 2: compute_rate<2><<<g, b, 0, s>>>(iters, seed, clk, sink); break;
+    default: compute_rate<3><<<g, b, 0, s>>>(iters, seed, clk, sink); break;
+    }
+    return -(int)hipGetLastError();
+}
+
+extern "C" int moe_probe_ticket_read(const void *buf, size_t bytes, int32_t blocks, int32_t mode,
+                                     uint32_t *counters, uint32_t *sink, void *hip_stream)
+{
+    const size_t unit = (size_t)kUnit16 * 16;
+    if (!buf || !counters || !sink || ((uintptr_t)buf % 16) || bytes % unit || bytes / unit == 0 ||
+        bytes / unit > 0xFFFFFFFFu || blocks < 1 || mode < 0 || mode > 2)
+        return -(int)hipErrorInvalidValue;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    hipError_t e = hipMemsetAsync(counters, 0, 8 * 32 * sizeof(uint32_t), s);
+    if (e != hipSuccess)
+        return -(int)e;
+    const uint32_t units = (uint32_t)(bytes / unit);
+    const u32x4 *p = (const u32x4 *)buf;
+    const dim3 g(blocks), b(256);
+    switch (mode) {
+    case 0: ticket_read<0><<<g, b, 0, s>>>(p, units, counters, sink); break;
+    case 1: ticket_read<1><<<g, b, 0, s>>>(p, units, counters, sink); break;
+    default: ticket_read<2><<<g, b, 0, s>>>(p, units, counters, sink); break;
+    }
+    return -(int)hipGetLastError();
+}
 
 extern "C" int moe_probe_stream_read(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink,
                                      void *hip_stream)

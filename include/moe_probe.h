@@ -2,14 +2,17 @@
  * moe_probe.h -- measurement probes that bench.py reports beside the decode
  * step's numbers on AMD Instinct MI355X (gfx950): the achievable HBM read
  * bandwidth of a plain streaming read, the launch floor of near-empty
- * kernels, and the LDS read rate of the MFMA operand pattern per staging
- * layout. They compute nothing of the decode step. The pages bound their
+ * kernels, the LDS read rate of the MFMA operand pattern per staging
+ * layout, the issue rates of the decode step's decode and MFMA halves on
+ * register operands, and a streaming read whose work units are claimed from
+ * shared counters. None of them computes a layer. The pages bound their
  * own kernel by the cold-read rate of their card, measured with a variant
  * that reads the weights without decoding them (page "LNA-CANON.md",
  * section "lna2 とは").
  *
  * Conventions: device pointers are plain device addresses; `hip_stream` is a
- * hipStream_t (NULL = default stream). Functions only enqueue work and return
+ * hipStream_t (NULL = default stream). Functions only enqueue work (kernels,
+ * and for moe_probe_ticket_read a memset of the caller's counters) and return
  * 0, or a negative HIP error code from the launch. No allocation.
  */
 #ifndef MOE_PROBE_H
@@ -50,6 +53,41 @@ int moe_probe_empty_kernels(int32_t count, void *hip_stream);
  */
 int moe_probe_lds_read128(int32_t layout, int32_t blocks, int32_t iters, uint32_t *sink,
                           void *hip_stream);
+
+/*
+ * Issue rates of the decode step's halves, on register operands only (no
+ * memory traffic): `blocks` blocks of 256 threads (4 waves), each wave
+ * running `iters` rounds of one 128-column group of a 3-bit codebook tile
+ * (4 MFMA 16x16x32 steps of 8 weights per lane) with the decode kernels' own
+ * decode instruction sequence. mode 0: decode only (each step's output
+ * xor-folded: 4 more VALU ops per step); 1: MFMA only (fixed B operand) and
+ * the group-scale FMAs; 2: decode into the MFMA and the group-scale FMAs (the
+ * decode kernels' inner step); 3: decode into four v_dot2_f32_f16 per step
+ * for one token (products on the VALU instead of the MFMA, the R = 1
+ * alternative). Every mode also changes the slot words each round (3 VALU
+ * ops). `clk` (device, 4 x u64): block 0's shader clock (s_memtime) and 100 MHz
+ * constant clock (s_memrealtime) before and after its rounds, from which the
+ * caller derives the clock rate; `sink` as for moe_probe_stream_read.
+ * Returns -hipErrorInvalidValue for a mode outside 0..3, blocks < 1,
+ * iters < 1 or a NULL clk or sink.
+ */
+int moe_probe_compute_rate(int32_t mode, int32_t blocks, int32_t iters, unsigned long long *clk,
+                           uint32_t *sink, void *hip_stream);
+
+/*
+ * The cost of claiming work from shared counters: `bytes` bytes at `buf`
+ * (16-byte aligned, a positive multiple of 64 KiB) read once in 64 KiB
+ * units by `blocks` blocks of 256 threads, one unit at a time (16 loads of
+ * 16 bytes per thread, all in flight). mode 0: block b reads units b, b + G,
+ * ... (static order); 1: every unit claimed from one counter (an agent-scope
+ * atomic add by the block's first thread, handed on through LDS); 2: from
+ * eight counters 128 bytes apart (block b claims from counter b % 8).
+ * `counters` (device, 1 KiB) is cleared by an enqueued memset before the
+ * kernel; `sink` as for moe_probe_stream_read. Returns -hipErrorInvalidValue
+ * for a bad size, alignment, mode or pointer.
+ */
+int moe_probe_ticket_read(const void *buf, size_t bytes, int32_t blocks, int32_t mode,
+                          uint32_t *counters, uint32_t *sink, void *hip_stream);
 
 #ifdef __cplusplus
 }

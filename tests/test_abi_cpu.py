@@ -35,7 +35,8 @@ def test_probe_library_exports_every_declared_function():
     """include/moe_probe.h (measurement probes) against libmoeprobe.so."""
     src = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_\w+)\(", src, re.M)))
-    assert names == ["moe_probe_empty_kernels", "moe_probe_lds_read128", "moe_probe_stream_read"]
+    assert names == ["moe_probe_compute_rate", "moe_probe_empty_kernels", "moe_probe_lds_read128",
+                     "moe_probe_stream_read", "moe_probe_ticket_read"]
     L = C.CDLL(os.path.join(ROOT, "bit_quantized_moe_block_amd", "libmoeprobe.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -46,6 +47,18 @@ def test_probe_library_exports_every_declared_function():
     assert L.moe_probe_stream_read(FAKE, 17, 4, FAKE, None) < 0
     assert L.moe_probe_stream_read(None, 16, 4, FAKE, None) < 0
     assert L.moe_probe_stream_read(FAKE, 16, 0, FAKE, None) < 0
+    L.moe_probe_compute_rate.restype = C.c_int
+    L.moe_probe_compute_rate.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                         C.c_void_p]
+    assert L.moe_probe_compute_rate(4, 1, 1, FAKE, FAKE, None) < 0   # no such mode
+    assert L.moe_probe_compute_rate(0, 0, 1, FAKE, FAKE, None) < 0   # no blocks
+    assert L.moe_probe_compute_rate(0, 1, 1, None, FAKE, None) < 0   # no clock buffer
+    L.moe_probe_ticket_read.restype = C.c_int
+    L.moe_probe_ticket_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
+                                        C.c_void_p, C.c_void_p]
+    assert L.moe_probe_ticket_read(FAKE, 65536 + 16, 4, 0, FAKE, FAKE, None) < 0  # not whole units
+    assert L.moe_probe_ticket_read(FAKE, 65536, 4, 3, FAKE, FAKE, None) < 0       # no such mode
+    assert L.moe_probe_ticket_read(FAKE, 65536, 4, 0, None, FAKE, None) < 0       # no counters
 
 
 def test_header_constants_match_binding():
