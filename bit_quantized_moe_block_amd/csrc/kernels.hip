@@ -701,11 +701,12 @@ __device__ __forceinline__ void set_prio(int p)
     }
 }
 
-// Groups 0..NG-1 of a row block. Gate/up items (their h is what down items
-// wait for) run above down items: before group j a gate/up wave takes
-// priority 1 + (rot + j) mod 3, rot = the block's residency slot on its CU,
-// so the gate/up blocks of a CU rotate through the levels instead of the
-// oldest always going first; down items take priority 0.
+// Groups 0..NG-1 of a row block. Before group j a gate/up wave takes
+// priority (rot + j) mod 4, rot = the block's residency slot on its CU (0..3),
+// so the four gate/up blocks of a CU take turns at each level instead of the
+// oldest always going first (the arbiter's order among equal priorities);
+// down items take priority 0, where the gate/up work (whose h they wait for)
+// meets them a quarter of the time.
 template <int CLASS, int NG, typename After>
 __device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLASS> &bB, int bits,
                                               const _Float16 *Arow, const uint32_t (&tab)[4],
@@ -714,7 +715,7 @@ __device__ __forceinline__ void compute_chunk(GroupBuf<CLASS> &bA, GroupBuf<CLAS
 {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-        set_prio(down ? 0 : 1 + (rot + j) % 3);
+        set_prio(down ? 0 : (rot + j) & 3);
         GroupBuf<CLASS> &b = (j & 1) ? bB : bA;
         process_any<CLASS>(b, j, bits, Arow, tab, lbase, acc);
         after(j, b);
@@ -1178,7 +1179,7 @@ void expert_kernel(Params p)
     int ticket = blockIdx.x;
     // residency slot: blocks b, b + C, b + 2C, ... (C = grid / blocks per CU)
     // share a CU, dispatched in that order
-    const int rot = uniform((int)(blockIdx.x / max(1u, gridDim.x / 4u))) % 3;
+    const int rot = uniform((int)(blockIdx.x / max(1u, gridDim.x / 4u))) & 3;
     Item cur = make_item(p, n_items, n_items1, n_sg, n_wide, s_grp, ticket);
     int pair = load_pair(p, cur, r16);
     uint32_t done = 0;
