@@ -40,13 +40,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-MoE decode µs/launch + achieved HBM GB/s of weight bytes, m=1–24"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "bit_quantized_moe_block_amd", "csrc", "kernels.hip")
+# the device code of the decode kernels: the kernel file, then the decode step it includes
+KERNEL_SRC = [os.path.join(ROOT, "bit_quantized_moe_block_amd", "csrc", f)
+              for f in ("kernels.hip", "decode_step.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_kernel_stack43_m16_traffic.md")
 
 
 def kernel_source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic():
