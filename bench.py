@@ -156,6 +156,18 @@ PROBE_LIB = os.path.join(ROOT, "bit_quantized_moe_block_amd", "libmoeprobe.so")
 _probe = None
 
 
+def _tile_stream_type():
+    import ctypes as C
+
+    class T(C.Structure):
+        _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("tile_rows", C.c_int32),
+                    ("groups", C.c_int32), ("bits", C.c_int32), ("units_before", C.c_int32)]
+    return T
+
+
+ProbeTileStream = _tile_stream_type()  # moe_probe_tile_stream of include/moe_probe.h
+
+
 def probe_lib():
     """The measurement probes of include/moe_probe.h (a library of their own)."""
     global _probe
@@ -173,6 +185,9 @@ def probe_lib():
         L.moe_probe_compute_rate.restype = C.c_int
         L.moe_probe_compute_rate.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                              C.c_void_p, C.c_void_p]
+        L.moe_probe_tile_read.restype = C.c_int
+        L.moe_probe_tile_read.argtypes = [C.POINTER(ProbeTileStream), C.c_int32, C.c_void_p,
+                                          C.c_int32, C.c_void_p, C.c_void_p]
         L.moe_probe_ticket_read.restype = C.c_int
         L.moe_probe_ticket_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32,
                                             C.c_void_p, C.c_void_p, C.c_void_p]
@@ -311,6 +326,56 @@ def probe_tickets(dev, mib=1024, reps=3):
     return out
 
 
+def probe_null_decode(dev, layers, hit_lists, stream, blocks=None, reps=3):
+    """The pages' null-decode measurement: the hit-expert matrices of every
+    resident layer (the weight bytes of the timed step) read with the expert
+    kernel's per-lane tile loads and nothing decoded, all layers in one launch
+    of moe_probe_tile_read (the 32-byte-per-matrix table upload it enqueues
+    first is inside the timed interval). Best of `reps` launches after one
+    warm-up. None when a layer holds a code width the probe does not read."""
+    import torch
+    L = probe_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = blocks or 4 * cus
+    rows, nbytes = [], 0
+    for layer, experts in zip(layers, hit_lists):
+        es = list(experts) + ([layer.E] if layer.has_shared else [])
+        for e in es:
+            for pj in range(3):
+                d = layer.descs[3 * int(e) + pj]
+                bits = int(d.bits)
+                if bits not in (2, 3, 4):
+                    return None
+                n, c = (layer.I, layer.H) if pj < 2 else (layer.H, layer.I)
+                rows.append((d.codes, d.scales, n // 16, c // 128, bits))
+    table = (ProbeTileStream * len(rows))()
+    before = 0
+    for i, (codes, scales, tr, g, bits) in enumerate(rows):
+        table[i] = ProbeTileStream(codes, scales, tr, g, bits, before)
+        before += (tr // 4) * (g // 8)
+        nbytes += tr * g * (256 * bits + (128 if bits == 4 else 32))
+    dev_tab = torch.zeros(len(rows) * 32, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 1e30
+    with torch.cuda.stream(stream):
+        for i in range(reps + 1):
+            e0.record(stream)
+            rc = L.moe_probe_tile_read(table, len(rows), dev_tab.data_ptr(), blocks, sink.data_ptr(),
+                                       stream.cuda_stream)
+            e1.record(stream)
+            if rc:
+                raise RuntimeError(f"moe_probe_tile_read: HIP error {-rc}")
+            stream.synchronize()
+            if i:
+                best = min(best, e0.elapsed_time(e1))
+    n_layers = len(hit_lists)
+    gbs = nbytes / (best * 1e-3) / 1e9
+    return {"us_per_layer": round(best * 1e3 / n_layers, 2), "gbs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_layer": int(nbytes / n_layers),
+            "matrices": len(rows), "blocks": blocks}
+
+
 def probe_launch_floor(dev, layers, reps=50):
     """The graph-replay floor of the step's launch structure: three empty
     kernels per layer (route, expert, combine), `layers` layers, in one graph.
@@ -420,11 +485,12 @@ def main():
             for layer, (x, lg, out) in zip(layers, io):
                 layer.run(x, lg, out, stream=stream)
         stream.synchronize()
-        wbytes, hit = [], []
+        wbytes, hit, hit_lists = [], [], []
         for layer in layers:
             b = layer.buckets(mm)
             experts = np.nonzero(b["counts"])[0]
             hit.append(len(experts))
+            hit_lists.append(experts)
             if layer.has_shared:  # the shared expert (stored as expert E) reads its weights too
                 experts = np.append(experts, layer.E)
             wbytes.append(layer.weight_bytes(experts))
@@ -493,7 +559,8 @@ def main():
         achieved = float(np.mean(kern_bytes)) / (kern_avg_ms * 1e-3) / 1e9
         r = {"m": mm, "ms_per_step": ms, "wall_ms": wall, "us_per_layer": ms * 1e3 / n_layers,
              "gbs": step_bytes / (ms * 1e-3) / 1e9, "step_bytes": step_bytes,
-             "hit": float(np.mean(hit)), "kernel_us": kern_avg_ms * 1e3, "kernel_gbs": achieved,
+             "hit": float(np.mean(hit)), "hit_lists": hit_lists,
+             "kernel_us": kern_avg_ms * 1e3, "kernel_gbs": achieved,
              "kernel_bytes": float(np.mean(kern_bytes))}
         log(f"m {mm}: step {ms:.3f} ms (wall {wall:.3f} ms), {r['us_per_layer']:.1f} us/layer, "
             f"{r['gbs']:.0f} GB/s; expert kernel {r['kernel_us']:.1f} us, {achieved:.0f} GB/s "
@@ -524,11 +591,12 @@ def main():
         floor = probe_launch_floor(dev, max(n_layers, 1))
         rates = probe_compute_rates(dev)
         tickets = probe_tickets(dev)
+        nd = probe_null_decode(dev, layers, head["hit_lists"], stream)
         probes = {"plain_read_gbs": round(gbs, 1), "plain_read_frac": round(gbs / HBM_PEAK_GBS, 4),
                   "plain_read_grid": grid,
                   "launch_floor_us_per_layer": round(floor, 2),
                   "launch_floor_kernels": 3 * max(n_layers, 1),
-                  "compute_rates": rates, "ticket_read": tickets}
+                  "compute_rates": rates, "ticket_read": tickets, "null_decode": nd}
         log(f"probes: plain read {gbs:.0f} GB/s ({grid} blocks), launch floor "
             f"{floor:.2f} us per layer (3 empty kernels per layer in one graph)")
         for r in rates:
@@ -536,6 +604,9 @@ def main():
                 f"({r['ns_per_step']} ns, clock {r['clock_ghz']} GHz)")
         for r in tickets:
             log(f"probes: streaming read, {r['desc']}: {r['gbs']} GB/s ({r['grid']} blocks)")
+        if nd:
+            log(f"probes: null decode (the expert kernels' weight reads, no decode) at m = {m}: "
+                f"{nd['us_per_layer']} us per layer, {nd['gbs']} GB/s ({nd['frac']:.1%} of 8 TB/s)")
 
     # ---- CPU oracle on a bounded sample (layer 0 of the workload, all m
     # tokens when m <= 24, else the first 16): median of 5 runs after one

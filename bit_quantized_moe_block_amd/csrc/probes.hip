@@ -13,6 +13,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Each thread walks the buffer with a grid-wide stride, four 16-byte loads
 // per round in flight, and xor-folds what it read.
@@ -199,7 +200,105 @@ __global__ __launch_bounds__(256) void ticket_read(const u32x4 *__restrict__ buf
         sink[0] = f;
 }
 
+// The weight reads of the decode kernels without the decode: each wave
+// streams work units of one stored matrix (4 tile rows x 8 column groups of
+// 16 x 128 weights: one wave's share of an expert-kernel item) in the
+// kernel's order, per group the 4 tiles' slot words (one load per tile at the
+// lane's slot offset, the kernel's load width for the code width) and their
+// scales (one 2-byte load per tile), two groups in flight, and xor-folds what
+// it read. Units are taken in a static order across the concatenated
+// matrices (wave w of the grid: units w, w + W, ...).
+constexpr int kMaxTileStreams = 8192;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void tile_read(const moe_probe_tile_stream *__restrict__ st, int ns, uint32_t total_units,
+               uint32_t *sink)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t nw = gridDim.x * 4u;
+    const uint32_t gw = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t fold = 0;
+    int s = 0;
+    for (uint32_t U = gw; U < total_units; U += nw) {
+        // the matrix holding unit U (streams in order; U only grows)
+        while (s + 1 < ns && U >= (uint32_t)__builtin_amdgcn_readfirstlane(st[s + 1].units_before))
+            ++s;
+        const moe_probe_tile_stream T = st[s];
+        const int G = __builtin_amdgcn_readfirstlane(T.groups), bits = __builtin_amdgcn_readfirstlane(T.bits);
+        const uint32_t u = U - (uint32_t)__builtin_amdgcn_readfirstlane(T.units_before);
+        const int per_band = G / 8;
+        const int r0 = (int)(u / per_band) * 4, g0 = (int)(u % per_band) * 8;
+        const uint64_t cb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T.codes >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)T.codes);
+        const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T.scales >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)T.scales);
+        const int tbytes = 256 * bits, sbytes = bits == 4 ? 128 : 32;
+        const int ntiles = __builtin_amdgcn_readfirstlane(T.tile_rows) * G;
+        // sized to the matrix: the bytes a 2-bit lane's 12-byte load reads
+        // past the last tile read as zero, without touching memory
+        const __amdgpu_buffer_rsrc_t rc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)cb, 0, ntiles * tbytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)sb, 0, ntiles * sbytes, 0x00020000);
+        const int sc_lane = bits == 4 ? (lane & 15) * 8 + 2 * (lane >> 4) : (lane & 15) * 2;
+        uint32_t w[2][4][4];
+#pragma unroll
+        for (int g = 0; g < 8 + 2; ++g) {
+            if (g >= 2) {  // consume group g - 2
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    fold ^= w[g & 1][i][0] ^ w[g & 1][i][1] ^ w[g & 1][i][2] ^ w[g & 1][i][3];
+            }
+            if (g < 8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tile = (r0 + i) * G + g0 + g;
+                    uint32_t *d = w[g & 1][i];
+                    if (bits == 4) {
+                        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, tile * tbytes, 0);
+                        d[0] = v[0]; d[1] = v[1]; d[2] = v[2];
+                    } else {
+                        // one 12-byte load for 2- and 3-bit tiles (the 2-bit lane's last 4 bytes unused)
+                        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 4 * bits, tile * tbytes, 0);
+                        d[0] = v[0]; d[1] = v[1]; d[2] = v[2];
+                    }
+                    d[3] = __builtin_amdgcn_raw_buffer_load_b16(rs, sc_lane, tile * sbytes, 0);
+                }
+            }
+        }
+    }
+    if (fold == 0x9E3779B9u)
+        sink[0] = fold;
+}
+
 }  // namespace
+
+extern "C" int moe_probe_tile_read(const moe_probe_tile_stream *streams, int32_t count,
+                                   moe_probe_tile_stream *dev_streams, int32_t blocks,
+                                   uint32_t *sink, void *hip_stream)
+{
+    if (!streams || !dev_streams || !sink || count < 1 || count > kMaxTileStreams || blocks < 1)
+        return -(int)hipErrorInvalidValue;
+    uint64_t units = 0;
+    for (int i = 0; i < count; ++i) {
+        const moe_probe_tile_stream &t = streams[i];
+        const uint64_t bytes = (uint64_t)t.tile_rows * (uint64_t)t.groups * 256u * (uint64_t)t.bits;
+        if (!t.codes || !t.scales || t.tile_rows < 4 || t.tile_rows % 4 || t.groups < 8 ||
+            t.groups % 8 || !(t.bits == 2 || t.bits == 3 || t.bits == 4) ||
+            (uint64_t)t.units_before != units || bytes > 0x7FFFFFFFu)
+            return -(int)hipErrorInvalidValue;
+        units += (uint64_t)(t.tile_rows / 4) * (uint64_t)(t.groups / 8);
+    }
+    if (units > 0x7FFFFFFFu)
+        return -(int)hipErrorInvalidValue;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    hipError_t e = hipMemcpyAsync(dev_streams, streams, sizeof(moe_probe_tile_stream) * count,
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess)
+        return -(int)e;
+    tile_read<<<dim3(blocks), dim3(256), 0, s>>>(dev_streams, count, (uint32_t)units, sink);
+    return -(int)hipGetLastError();
+}
 
 extern "C" int moe_probe_compute_rate(int32_t mode, int32_t blocks, int32_t iters,
                                       unsigned long long *clk, uint32_t *sink, void *hip_stream)

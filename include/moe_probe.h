@@ -89,6 +89,38 @@ int moe_probe_compute_rate(int32_t mode, int32_t blocks, int32_t iters, unsigned
 int moe_probe_ticket_read(const void *buf, size_t bytes, int32_t blocks, int32_t mode,
                           uint32_t *counters, uint32_t *sink, void *hip_stream);
 
+/* One stored matrix for moe_probe_tile_read (the layout of the decode step's
+ * stored formats: tiles of 16 rows x 128 columns, `tile_rows` x `groups`
+ * tiles in row-block-major order, 256 * bits bytes each; scales per tile,
+ * 32 bytes (codebook) or 128 bytes (NVFP4, bits = 4)). */
+typedef struct moe_probe_tile_stream {
+    const void *codes;     /* device address of the matrix's first tile */
+    const void *scales;    /* device address of its first tile's scales */
+    int32_t tile_rows;     /* rows / 16, a positive multiple of 4 */
+    int32_t groups;        /* columns / 128, a positive multiple of 8 */
+    int32_t bits;          /* 2 or 3 (codebook codes), 4 (NVFP4) */
+    int32_t units_before;  /* work units of the matrices before this one
+                              (a unit: 4 tile rows x 8 groups) */
+} moe_probe_tile_stream;
+
+/*
+ * The decode kernels' weight reads without the decode (the pages' null-decode
+ * measurement, "LNA-CANON.md" §"lna2 とは"): `count` (1..8192) stored
+ * matrices, described in the host array `streams`, read once by `blocks`
+ * blocks of 4 waves. Each wave takes units of 4 tile rows x 8 column groups
+ * (one wave's share of an expert-kernel item) in a static order across the
+ * matrices and reads them as the expert kernel does: per group one load of
+ * the lane's slot words per tile (12 bytes for 2- and 3-bit tiles, 16 for
+ * NVFP4) and one 2-byte scale load per tile, two groups in flight; the words
+ * are xor-folded. The table is copied (enqueued) to `dev_streams` (device,
+ * count x 32 bytes); `sink` as for moe_probe_stream_read. Returns
+ * -hipErrorInvalidValue for a bad count, block count, pointer, shape, width,
+ * units_before (must be the running sum) or a matrix of 2 GiB or more.
+ */
+int moe_probe_tile_read(const moe_probe_tile_stream *streams, int32_t count,
+                        moe_probe_tile_stream *dev_streams, int32_t blocks, uint32_t *sink,
+                        void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def test_probe_library_exports_every_declared_function():
     src = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_\w+)\(", src, re.M)))
     assert names == ["moe_probe_compute_rate", "moe_probe_empty_kernels", "moe_probe_lds_read128",
-                     "moe_probe_stream_read", "moe_probe_ticket_read"]
+                     "moe_probe_stream_read", "moe_probe_ticket_read", "moe_probe_tile_read"]
     L = C.CDLL(os.path.join(ROOT, "bit_quantized_moe_block_amd", "libmoeprobe.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -59,6 +59,23 @@ def test_probe_library_exports_every_declared_function():
     assert L.moe_probe_ticket_read(FAKE, 65536 + 16, 4, 0, FAKE, FAKE, None) < 0  # not whole units
     assert L.moe_probe_ticket_read(FAKE, 65536, 4, 3, FAKE, FAKE, None) < 0       # no such mode
     assert L.moe_probe_ticket_read(FAKE, 65536, 4, 0, None, FAKE, None) < 0       # no counters
+    import bench
+    T = bench.ProbeTileStream
+    assert C.sizeof(T) == 32
+    L.moe_probe_tile_read.restype = C.c_int
+    L.moe_probe_tile_read.argtypes = [C.POINTER(T), C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                      C.c_void_p]
+    good = T(FAKE, FAKE, 128, 32, 3, 0)
+    for bad in (T(FAKE, FAKE, 126, 32, 3, 0),   # tile rows not a multiple of 4
+                T(FAKE, FAKE, 128, 12, 3, 0),   # groups not a multiple of 8
+                T(FAKE, FAKE, 128, 32, 6, 0),   # a width the probe does not read
+                T(None, FAKE, 128, 32, 3, 0),   # no codes
+                T(FAKE, FAKE, 128, 32, 3, 5)):  # units_before not the running sum
+        tab = (T * 2)(good, bad)
+        tab[1].units_before = bad.units_before if bad.units_before else 32 * 4
+        assert L.moe_probe_tile_read(tab, 2, FAKE, 4, FAKE, None) < 0
+    assert L.moe_probe_tile_read((T * 1)(good), 0, FAKE, 4, FAKE, None) < 0        # no matrices
+    assert L.moe_probe_tile_read((T * 1)(good), 1, None, 4, FAKE, None) < 0        # no device table
 
 
 def test_header_constants_match_binding():
