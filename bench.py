@@ -47,10 +47,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_kernel_stack43_m16_traffic
 
 
 def kernel_source_sha():
+    """sha256 of the decode kernels' code: the files of KERNEL_SRC in order,
+    comments removed and whitespace runs collapsed (an edit to a comment
+    leaves the counters of the same code valid)."""
     h = hashlib.sha256()
     for path in KERNEL_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

@@ -16,6 +16,10 @@
 //                items (256 rows of down, one column split) wait on a
 //                per-group counter of finished h blocks and store their
 //                partial sums under the pair index.
+// small_kernel   runs of at most 4 tokens whose items fit one round of the
+//                grid: gate/up items of 32 rows over all columns (whole
+//                sums: SiLU(g)*u in the item), down items of 64 rows that
+//                rotate h themselves after their group's h counter is full.
 // combine_kernel one wave per (token, 256-row block): the down partial sums
 //                of the token's k slots, in slot order, times the router
 //                weights (NaN if the expert kernel reported an error).
